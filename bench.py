@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one pass of the whole hot path over one batch: fa_fwd, then the three
+backward kernels (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), on synthetic seeded
+inputs already resident in HBM. The default workload is the Llama-shaped causal case
+(B=4, H=32, N=4096, d=128, bf16). Prints one JSON line.
+
+FLOP model (algorithmic work, not what the kernels happen to execute): one "GEMM
+unit" is 2*B*H*N^2*d, halved under causal masking. Forward = 2 units (QK^T, PV);
+backward = 5 units (recomputed QK^T, dO V^T, P^T dO, dS^T Q, dS K), i.e. 2.5x the
+forward. Per kernel: fwd 2 units, dkdv 4, dq 1 (its recomputation of S and dP is the
+price of a dQ pass without atomics and is not counted), preprocess 0.
+
+The CPU baseline times the fp64 oracle on a bounded sample of the same workload
+(whole heads, forward + backward), on the host cores, and reports the same FLOP
+model per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s, bf16 d=128 N=4096 causal; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_unit(B, H, N, d, causal, lengths=None):
+    if lengths is not None:
+        return sum(2.0 * H * L * L * d * (0.5 if causal else 1.0) for L in lengths)
+    return 2.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+
+
+def cpu_baseline(inp, w, budget_s: float):
+    """Time the oracle (fp64, NumPy) on whole heads of the workload until ~budget_s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = len(os.sched_getaffinity(0))
+    B, H = inp.q.shape[0], inp.q.shape[2]
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        q, k, v, do = (oracle.to_f64(t[b, :, h, :]) for t in (inp.q, inp.k, inp.v, inp.do))
+        oracle.head_forward(q, k, v, w.scale, w.causal)
+        oracle.head_backward(q, k, v, do, w.scale, w.causal)
+        N, d = q.shape
+        flops += 7 * gemm_unit(1, 1, N, d, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs of {w.name}, fp64 forward + backward "
+                  f"(oracle materialises the full N x N scores), {dt:.1f} s wall",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the attention path has no "
+              "cross-GPU component; see the sharding notes in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_io_aware_attention_amd as fa
+    import workloads as W
+
+    fa.load_library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    w = W.get(a.workload)
+    log(f"bench: generating {w.name} inputs")
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
+    cu = inp.cu_seqlens.to(dev) if inp.cu_seqlens is not None else None
+    B, N, H, d, T = inp.batch, inp.seqlen, w.heads, w.head_dim, inp.total_tokens
+    dt_code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_FP32
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N) if cu is None else (H, T), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_bytes(B, H, N, d, int(cu is not None), T)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    cup = cu.data_ptr() if cu is not None else None
+    causal = int(w.causal)
+
+    def check(st, name):
+        if st != fa.FA_OK:
+            raise fa.FAError(st, name)
+
+    def k_fwd():
+        check(fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                        w.scale, causal, cup, T, dt_code, sp), "fa_fwd")
+
+    def k_pre():
+        check(fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d, cup, T,
+                                   dt_code, sp), "fa_bwd_preprocess")
+
+    def k_dkdv():
+        check(fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             ws.data_ptr(), ws_bytes, dk.data_ptr(), dv.data_ptr(), B, H, N, d, w.scale,
+                             causal, cup, T, dt_code, sp), "fa_bwd_dkdv")
+
+    def k_dq():
+        check(fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                           ws.data_ptr(), ws_bytes, dq.data_ptr(), B, H, N, d, w.scale, causal, cup, T,
+                           dt_code, sp), "fa_bwd_dq")
+
+    kernels = [("fwd", k_fwd), ("bwd_preprocess", k_pre), ("bwd_dkdv", k_dkdv), ("bwd_dq", k_dq)]
+    log(f"bench: warmup {a.warmup}")
+    for _ in range(a.warmup):
+        for _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(a.steps)]
+    log(f"bench: timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(kernels):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(a.steps)) / a.steps
+           for i, (name, _) in enumerate(kernels)}
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(a.steps)) / a.steps
+    log("bench: per-kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in per.items()}))
+
+    unit = gemm_unit(B, H, N, d, w.causal, inp.lengths)
+    fwd_fl, bwd_fl = 2 * unit, 5 * unit
+    algo = {"fwd": 2 * unit, "bwd_preprocess": 0.0, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    value = (fwd_fl + bwd_fl) / (step_ms * 1e-3) / 1e12
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
+    achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid normal inputs)",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": bool(w.causal),
+            "global_batch": B, "parallelism": "single GPU",
+        },
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(per["fwd"], 4), "tflops": round(fwd_fl / (per["fwd"] * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(fwd_fl / (per["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in per.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if a.cpu_budget > 0 and w.varlen is False:
+        log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

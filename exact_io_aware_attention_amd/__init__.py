@@ -1,0 +1,201 @@
+"""exact_io_aware_attention_amd: exact IO-aware attention on AMD MI355X (gfx950).
+
+A thin Python binding over ``libfa.so``, whose C ABI is declared in ``include/fa.h``.
+The raw entry points keep the C names and take integer device pointers:
+
+    fa_fwd, fa_bwd, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_workspace_bytes,
+    fa_strerror
+
+``forward`` and ``backward`` marshal torch tensors (device memory and the current
+stream) into those calls; every step of the computation runs in the HIP kernels.
+There is no fallback: if ``libfa.so`` is missing or fails to load, every call raises.
+Build it with ``python -m exact_io_aware_attention_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
+    "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
+    "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
+    "fa_strerror", "forward", "backward",
+]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status}: {fa_strerror(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m exact_io_aware_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                           i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i32, i32, i32, i32, vp, i32, i32, vp]
+    lib.fa_bwd_preprocess.restype = i32
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
+    lib.fa_bwd_dkdv.restype = i32
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
+    lib.fa_bwd_dq.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_strerror.argtypes = [i32]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------- raw C entry points
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, batch: int, heads: int, seqlen: int,
+           head_dim: int, softmax_scale: float, causal: int, cu_seqlens: Optional[int],
+           total_tokens: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_fwd(q, k, v, o, lse, batch, heads, seqlen, head_dim, softmax_scale,
+                                 int(causal), cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+           workspace: int, workspace_bytes: int, batch: int, heads: int, seqlen: int, head_dim: int,
+           softmax_scale: float, causal: int, cu_seqlens: Optional[int], total_tokens: int,
+           dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                                 batch, heads, seqlen, head_dim, softmax_scale, int(causal),
+                                 cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd_preprocess(o: int, dout: int, workspace: int, workspace_bytes: int, batch: int, heads: int,
+                      seqlen: int, head_dim: int, cu_seqlens: Optional[int], total_tokens: int, dtype: int,
+                      stream: Optional[int]) -> int:
+    return load_library().fa_bwd_preprocess(o, dout, workspace, workspace_bytes, batch, heads, seqlen,
+                                            head_dim, cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd_dkdv(q: int, k: int, v: int, dout: int, lse: int, workspace: int, workspace_bytes: int,
+                dk: int, dv: int, batch: int, heads: int, seqlen: int, head_dim: int, softmax_scale: float,
+                causal: int, cu_seqlens: Optional[int], total_tokens: int, dtype: int,
+                stream: Optional[int]) -> int:
+    return load_library().fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, batch, heads,
+                                      seqlen, head_dim, softmax_scale, int(causal), cu_seqlens, total_tokens,
+                                      dtype, stream)
+
+
+def fa_bwd_dq(q: int, k: int, v: int, dout: int, lse: int, workspace: int, workspace_bytes: int, dq: int,
+              batch: int, heads: int, seqlen: int, head_dim: int, softmax_scale: float, causal: int,
+              cu_seqlens: Optional[int], total_tokens: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen,
+                                    head_dim, softmax_scale, int(causal), cu_seqlens, total_tokens, dtype,
+                                    stream)
+
+
+def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen: int, head_dim: int, varlen: int,
+                           total_tokens: int) -> int:
+    return load_library().fa_bwd_workspace_bytes(batch, heads, seqlen, head_dim, int(varlen), total_tokens)
+
+
+def fa_strerror(status: int) -> str:
+    return load_library().fa_strerror(status).decode()
+
+
+# ---------------------------------------------------------------- torch marshalling
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _shape(q, cu_seqlens, max_seqlen):
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("q must be (batch, seqlen, heads, head_dim)")
+        B, N, H, d = q.shape
+        return B, N, H, d, B * N
+    if q.dim() != 3:
+        raise ValueError("packed q must be (total_tokens, heads, head_dim)")
+    if max_seqlen is None:
+        raise ValueError("max_seqlen is required with cu_seqlens")
+    T, H, d = q.shape
+    return cu_seqlens.numel() - 1, int(max_seqlen), H, d, T
+
+
+def _check(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _stream(stream):
+    import torch
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, cu_seqlens=None,
+            max_seqlen: Optional[int] = None, out=None, lse=None, stream=None) -> Tuple:
+    """O and the fp32 natural-log LSE of exact attention (see include/fa.h)."""
+    import torch
+    B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
+    _check(q, k, v)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse_shape = (B, H, N) if cu_seqlens is None else (H, T)
+        lse = torch.empty(lse_shape, device=q.device, dtype=torch.float32)
+    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
+             cu_seqlens=None, max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None) -> Tuple:
+    """(dQ, dK, dV) for the upstream gradient ``dout`` (see include/fa.h)."""
+    import torch
+    B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
+    _check(q, k, v, o, lse, dout)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_bytes(B, H, N, d, int(cu_seqlens is not None), T)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
+    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                B, H, N, d, scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,192 @@
+// fa_api.hip - the C ABI of libfa.so: argument checks on the host, then kernel launches
+// on the caller's stream. Declarations and conventions: include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 16;
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+// Common checks of fa_fwd and fa_bwd; fills the sizes of `pr`.
+int check_common(int batch, int heads, int seqlen, int head_dim, float scale, int causal,
+                 const int32_t* cu_seqlens, int total_tokens, int dtype, fa::Problem& pr) {
+  if (batch < 1 || heads < 1 || seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  if (cu_seqlens != nullptr) {
+    if (total_tokens < 0) return FA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) % sizeof(int32_t) != 0) return FA_ERR_INVALID_ARG;
+  }
+  const long long tokens = cu_seqlens ? (long long)total_tokens : (long long)batch * seqlen;
+  // Element offsets are computed in 64 bits; the lse/D index (heads * tokens) and the
+  // launch grid (sequences * heads * tiles) must fit the kernels' 32-bit work counters.
+  if ((long long)heads * tokens > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if ((long long)batch * heads * ((seqlen + 63) / 64) > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (!cu_seqlens && tokens > INT32_MAX) return FA_ERR_INVALID_ARG;
+  pr.batch = batch;
+  pr.heads = heads;
+  pr.seqlen = seqlen;
+  pr.head_dim = head_dim;
+  pr.total_tokens = (int)tokens;
+  pr.scale = scale;
+  pr.causal = causal != 0;
+  pr.cu_seqlens = cu_seqlens;
+  return FA_OK;
+}
+
+// D: one fp32 per (head, token), rounded up to 256 bytes.
+size_t workspace_bytes_for(int heads, long long tokens) {
+  const size_t bytes = (size_t)heads * (size_t)tokens * sizeof(float);
+  return ((bytes + 255) / 256) * 256;
+}
+
+// Checks shared by the backward entry points; sets pr.dvec to the workspace.
+int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
+              int head_dim, float scale, int causal, const int32_t* cu_seqlens, int total_tokens, int dtype) {
+  const int st = check_common(batch, heads, seqlen, head_dim, scale, causal, cu_seqlens, total_tokens, dtype, pr);
+  if (st != FA_OK) return st;
+  const size_t need = workspace_bytes_for(heads, pr.total_tokens);
+  if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FA_ERR_WORKSPACE;
+  pr.dvec = static_cast<float*>(workspace);
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+#define FA_EXPORT __attribute__((visibility("default")))
+
+extern "C" {
+
+FA_EXPORT int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
+           int seqlen, int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,
+           int total_tokens, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse)) return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_common(batch, heads, seqlen, head_dim, softmax_scale, causal, cu_seqlens,
+                              total_tokens, dtype, pr);
+  if (st != FA_OK) return st;
+  if (pr.total_tokens == 0) return FA_OK;  // a packed batch of empty sequences
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.o_out = o;
+  pr.lse_out = lse;
+  pr.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(pr) : fa::launch_fwd_fp32(pr);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_EXPORT size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim, int varlen, int total_tokens) {
+  if (batch < 1 || heads < 1 || seqlen < 1) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  if (varlen && total_tokens < 0) return 0;
+  const long long tokens = varlen ? (long long)total_tokens : (long long)batch * seqlen;
+  return workspace_bytes_for(heads, tokens);
+}
+
+
+FA_EXPORT int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int batch,
+                      int heads, int seqlen, int head_dim, const int32_t* cu_seqlens, int total_tokens,
+                      int dtype, void* stream) {
+  if (!o || !dout) return FA_ERR_INVALID_ARG;
+  if (!aligned(o) || !aligned(dout)) return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, 1.f, 0,
+                           cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK || pr.total_tokens == 0) return st;
+  pr.o = o;
+  pr.dout = dout;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(fa::launch_bwd_pre(pr, dtype == FA_DTYPE_FP32));
+}
+
+FA_EXPORT int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv, int batch, int heads,
+                int seqlen, int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,
+                int total_tokens, int dtype, void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(dout) || !aligned(lse) || !aligned(dk) ||
+      !aligned(dv))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, const_cast<void*>(workspace), workspace_bytes, batch, heads, seqlen, head_dim,
+                           softmax_scale, causal, cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK || pr.total_tokens == 0) return st;
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.dout = dout;
+  pr.lse = lse;
+  pr.dk = dk;
+  pr.dv = dv;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dkdv_bf16(pr) : fa::launch_bwd_dkdv_fp32(pr));
+}
+
+FA_EXPORT int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const void* workspace, size_t workspace_bytes, void* dq, int batch, int heads, int seqlen,
+              int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens, int total_tokens,
+              int dtype, void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(dout) || !aligned(lse) || !aligned(dq))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, const_cast<void*>(workspace), workspace_bytes, batch, heads, seqlen, head_dim,
+                           softmax_scale, causal, cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK || pr.total_tokens == 0) return st;
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.dout = dout;
+  pr.lse = lse;
+  pr.dq = dq;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dq_bf16(pr) : fa::launch_bwd_dq_fp32(pr));
+}
+
+FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
+           int seqlen, int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,
+           int total_tokens, int dtype, void* stream) {
+  // Check everything before enqueueing anything, so a bad argument launches nothing.
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(dout) || !aligned(lse) ||
+      !aligned(dq) || !aligned(dk) || !aligned(dv))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale,
+                           causal, cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK || pr.total_tokens == 0) return st;
+  int r = fa_bwd_preprocess(o, dout, workspace, workspace_bytes, batch, heads, seqlen, head_dim, cu_seqlens,
+                            total_tokens, dtype, stream);
+  if (r != FA_OK) return r;
+  r = fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, batch, heads, seqlen, head_dim,
+                  softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+  if (r != FA_OK) return r;
+  return fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen, head_dim,
+                   softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+}
+
+FA_EXPORT const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or flag)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype (head_dim 64 or 128; bf16 or fp32)";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,451 @@
+// fa_bwd.hip - backward pass of exact attention, bf16 tensors, fp32 arithmetic (gfx950).
+//
+// P is never read from memory: every kernel recomputes it tile by tile from Q, K and
+// the saved logsumexp, P = exp2(c * q.k - LSE * log2(e)) with c = scale * log2(e)
+// ("Recalcular en vez de guardar" in the AI Atlas summary of the FlashAttention paper).
+// Three kernels:
+//   bwd_pre   D_i = sum_k dO_ik * O_ik for every query row (fp32), from the stored O.
+//   bwd_dkdv  one workgroup per (sequence, head, 128-key tile); each wave owns 32 keys
+//             and keeps K, V fragments and the dK^T, dV^T accumulators in registers
+//             while it walks the 64-query tiles:
+//                 S  = Q K^T,  P = exp2(c S - LSE log2e)
+//                 dP = dO V^T, dS = P * (dP - D)
+//                 dV^T += dO^T P,  dK^T += Q^T dS
+//             S and dP are computed with one key per MFMA column, so P and dS feed the
+//             next products' B operands straight from registers; Q and dO are staged
+//             in LDS both row-major and transposed for the A operands.
+//   bwd_dq    the dQ accumulation pass: one workgroup per (sequence, head, 128-query
+//             tile), dQ^T += K^T dS^T over the key tiles, with one query per MFMA column.
+// There are no atomics, so the result is bitwise reproducible run to run.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+struct BwdParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  const u16* o;
+  const u16* dout;
+  const float* lse;
+  const float* dvec;
+  float* dvec_out;
+  u16* dq;
+  u16* dk;
+  u16* dv;
+  const int32_t* cu;
+  int B, H, N, T;
+  int n_tiles;  // query tiles (dq) or key tiles (dkdv) per sequence
+  float scale;
+  float c;      // scale * log2(e)
+};
+
+// Index of (sequence b, head h, sequence-relative row n) in the lse / D layout:
+// (B, H, N) for padded batches, (H, T) for packed ones.
+template <bool VARLEN>
+__device__ __forceinline__ size_t stat_index(const BwdParams& p, int b, int h, int start, int n) {
+  return VARLEN ? (size_t)h * p.T + start + n : ((size_t)b * p.H + h) * p.N + n;
+}
+
+// ------------------------------------------------------------------------ bwd_pre
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out);
+
+template <>
+__device__ __forceinline__ void load8<u16>(const u16* p, float* out) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(x[i] << 16);
+    out[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* out) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = a[i];
+    out[4 + i] = b[i];
+  }
+}
+
+// One (token, head) row per D/8 lanes: rows are contiguous in memory, so a wave reads
+// a contiguous span of O and dO.
+template <int D, typename T, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                      float* __restrict__ dvec, int H, int N, int T_total,
+                                                      long long rows) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    float a[8], bq[8];
+    load8<T>(o + row * D + 8 * sub, a);
+    load8<T>(dout + row * D + 8 * sub, bq);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], bq[i], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && sub == 0) {
+    const long long token = row / H;
+    const int h = (int)(row % H);
+    const size_t idx = VARLEN ? (size_t)h * T_total + token
+                              : ((size_t)(token / N) * H + h) * N + (size_t)(token % N);
+    dvec[idx] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------ bwd_dkdv
+
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
+constexpr int kKvBQ = 64;             // queries per tile
+constexpr int kPadRow = 8;
+constexpr int kPadT = 8;
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
+  constexpr int BK = kKvBK, BQ = kKvBQ, NT = kKvThreads;
+  constexpr int NB = D / 32;    // 32-wide head-dim blocks of dK^T / dV^T
+  constexpr int NS = D / 16;    // k-steps over the head dim
+  constexpr int NA = BQ / 32;   // 32-query blocks of S per tile
+  constexpr int NTQ = BQ / 16;  // k-steps over the queries of a tile
+  constexpr int RP = D + kPadRow;
+  constexpr int TPITCH = BQ + kPadT;
+
+  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RP];
+  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RP];
+  __shared__ __attribute__((aligned(16))) u16 QT[D * TPITCH];
+  __shared__ __attribute__((aligned(16))) u16 dOT[D * TPITCH];
+  __shared__ __attribute__((aligned(16))) float lse_s[BQ];  // LSE * log2(e); +inf past the end
+  __shared__ __attribute__((aligned(16))) float dd_s[BQ];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+
+  // Workgroup -> (sequence, head, key tile); under causal the first key tiles see the
+  // most queries, and they come first in launch order already.
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int k0 = kt * BK;
+  if (k0 >= len) return;
+
+  const size_t stride = (size_t)p.H * D;
+  const size_t base = ((size_t)start * p.H + h) * D;
+  const u16* __restrict__ Qg = p.q + base;
+  const u16* __restrict__ dOg = p.dout + base;
+
+  const int wk0 = k0 + 32 * w;  // first key of this wave
+  const int kj = wk0 + lr;      // this lane's key
+
+  bf16x8 kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const size_t off = base + (size_t)kj * stride + 16 * s + 8 * g;
+    kf[s] = kj < len ? ld16(p.k + off) : zero_bf16x8();
+    vf[s] = kj < len ? ld16(p.v + off) : zero_bf16x8();
+  }
+
+  f32x16 dvT[NB], dkT[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    dvT[bb] = f32x16{};
+    dkT[bb] = f32x16{};
+  }
+
+  const int qt_begin = CAUSAL ? k0 / BQ : 0;
+  const int n_qt = (len + BQ - 1) / BQ;
+
+  for (int qt = qt_begin; qt < n_qt; ++qt) {
+    const int q0 = qt * BQ;
+    if (qt > qt_begin) __syncthreads();
+    stage_rows<BQ, D, kPadRow, NT>(Qs, Qg, q0, len, stride, tid);
+    stage_rows<BQ, D, kPadRow, NT>(dOs, dOg, q0, len, stride, tid);
+    stage_transposed<BQ, D, kPadT, NT>(QT, Qg, q0, len, stride, tid);
+    stage_transposed<BQ, D, kPadT, NT>(dOT, dOg, q0, len, stride, tid);
+    if (tid < BQ) {
+      const int qq = q0 + tid;
+      lse_s[tid] = qq < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e : INFINITY;
+      dd_s[tid] = qq < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qq)] : 0.f;
+    }
+    __syncthreads();
+
+    const bool active = wk0 < len && (!CAUSAL || q0 + BQ - 1 >= wk0);
+    if (!active) continue;
+
+    // S = Q K^T and dP = dO V^T with one key per column: register r of block a (lane
+    // group g) holds query q0 + 32a + crow_of_reg(r, g) against key kj.
+    f32x16 sacc[NA], dpacc[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      sacc[a] = f32x16{};
+      dpacc[a] = f32x16{};
+      const int arow = (32 * a + perm_rows(lr)) * RP + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc[a] = mfma32(ld16(Qs + arow + 16 * s), kf[s], sacc[a]);
+        dpacc[a] = mfma32(ld16(dOs + arow + 16 * s), vf[s], dpacc[a]);
+      }
+    }
+
+    const bool need_mask = CAUSAL && q0 < wk0 + 31;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = 32 * a + crow_of_reg(r, g);
+        float pv = fast_exp2(fmaf(sacc[a][r], p.c, -lse_s[qrow]));
+        if (need_mask && kj > q0 + qrow) pv = 0.f;
+        sacc[a][r] = pv;
+        dpacc[a][r] = pv * (dpacc[a][r] - dd_s[qrow]);
+      }
+    }
+
+    bf16x8 pb[NTQ], dsb[NTQ];
+#pragma unroll
+    for (int t = 0; t < NTQ; ++t) {
+      pb[t] = to_bf16x8(half_of(sacc[t >> 1], t & 1));
+      dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: A row m of block bb is head-dim entry
+    // 32bb + perm_cols(m); k-slots of lane group g at step t are queries 16t + 8g + 0..7.
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int arow = (32 * bb + perm_cols(lr)) * TPITCH + 8 * g;
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) {
+        dvT[bb] = mfma32(ld16(dOT + arow + 16 * t), pb[t], dvT[bb]);
+        dkT[bb] = mfma32(ld16(QT + arow + 16 * t), dsb[t], dkT[bb]);
+      }
+    }
+  }
+
+  if (kj >= len) return;
+  u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
+  u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    *reinterpret_cast<bf16x8*>(dKg + 32 * bb + 16 * g) = to_bf16x8(half_of(dkT[bb], 0) * p.scale);
+    *reinterpret_cast<bf16x8*>(dKg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dkT[bb], 1) * p.scale);
+    *reinterpret_cast<bf16x8*>(dVg + 32 * bb + 16 * g) = to_bf16x8(half_of(dvT[bb], 0));
+    *reinterpret_cast<bf16x8*>(dVg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dvT[bb], 1));
+  }
+}
+
+// ------------------------------------------------------------------------ bwd_dq
+
+constexpr int kDqWaves = 4;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqBR = 32 * kDqWaves;  // queries per workgroup
+constexpr int kDqBC = 64;             // keys per tile
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
+  constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
+  constexpr int NB = D / 32, NS = D / 16, NJ = BC / 32, NTK = BC / 16;
+  constexpr int RP = D + kPadRow;
+  constexpr int TPITCH = BC + kPadT;
+
+  __shared__ __attribute__((aligned(16))) u16 Ks[BC * RP];
+  __shared__ __attribute__((aligned(16))) u16 Vs[BC * RP];
+  __shared__ __attribute__((aligned(16))) u16 KT[D * TPITCH];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if (CAUSAL) qt = p.n_tiles - 1 - qt;
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int q0 = qt * BR;
+  if (q0 >= len) return;
+
+  const size_t stride = (size_t)p.H * D;
+  const size_t base = ((size_t)start * p.H + h) * D;
+  const u16* __restrict__ Kg = p.k + base;
+  const u16* __restrict__ Vg = p.v + base;
+
+  const int wq0 = q0 + 32 * w;
+  const int qi = wq0 + lr;
+  const int wq_last = min(wq0 + 31, len - 1);
+
+  bf16x8 qf[NS], dof[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const size_t off = base + (size_t)qi * stride + 16 * s + 8 * g;
+    qf[s] = qi < len ? ld16(p.q + off) : zero_bf16x8();
+    dof[s] = qi < len ? ld16(p.dout + off) : zero_bf16x8();
+  }
+  const float lse_i = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] * kLog2e : INFINITY;
+  const float d_i = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
+
+  f32x16 dqT[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) dqT[bb] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
+  const int n_kt = (kv_end + BC - 1) / BC;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BC;
+    if (kt > 0) __syncthreads();
+    stage_rows<BC, D, kPadRow, NT>(Ks, Kg, k0, len, stride, tid);
+    stage_rows<BC, D, kPadRow, NT>(Vs, Vg, k0, len, stride, tid);
+    stage_transposed<BC, D, kPadT, NT>(KT, Kg, k0, len, stride, tid);
+    __syncthreads();
+
+    const bool active = wq0 < len && (!CAUSAL || k0 <= wq_last);
+    if (!active) continue;
+
+    // S^T = K Q^T and dP^T = V dO^T with one query per column: register r of block j
+    // (lane group g) holds key k0 + 32j + crow_of_reg(r, g) against query qi.
+    f32x16 sacc[NJ], dpacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      sacc[j] = f32x16{};
+      dpacc[j] = f32x16{};
+      const int arow = (32 * j + perm_rows(lr)) * RP + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc[j] = mfma32(ld16(Ks + arow + 16 * s), qf[s], sacc[j]);
+        dpacc[j] = mfma32(ld16(Vs + arow + 16 * s), dof[s], dpacc[j]);
+      }
+    }
+
+    const bool need_mask = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > wq0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(sacc[j][r], p.c, -lse_i));
+        if (need_mask) {
+          const int key = k0 + 32 * j + crow_of_reg(r, g);
+          if (key >= len || (CAUSAL && key > qi)) pv = 0.f;
+        }
+        dpacc[j][r] = pv * (dpacc[j][r] - d_i);
+      }
+    }
+
+    bf16x8 dsb[NTK];
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
+    // dQ^T += K^T dS^T: A row m of block bb is head-dim entry 32bb + perm_cols(m);
+    // k-slots of lane group g at step t are keys 16t + 8g + 0..7.
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int arow = (32 * bb + perm_cols(lr)) * TPITCH + 8 * g;
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) dqT[bb] = mfma32(ld16(KT + arow + 16 * t), dsb[t], dqT[bb]);
+    }
+  }
+
+  if (qi >= len) return;
+  u16* __restrict__ dQg = p.dq + base + (size_t)qi * stride;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    *reinterpret_cast<bf16x8*>(dQg + 32 * bb + 16 * g) = to_bf16x8(half_of(dqT[bb], 0) * p.scale);
+    *reinterpret_cast<bf16x8*>(dQg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dqT[bb], 1) * p.scale);
+  }
+}
+
+// ------------------------------------------------------------------------ launch
+
+BwdParams make_params(const Problem& pr) {
+  BwdParams p;
+  p.q = static_cast<const u16*>(pr.q);
+  p.k = static_cast<const u16*>(pr.k);
+  p.v = static_cast<const u16*>(pr.v);
+  p.o = static_cast<const u16*>(pr.o);
+  p.dout = static_cast<const u16*>(pr.dout);
+  p.lse = pr.lse;
+  p.dvec = pr.dvec;
+  p.dvec_out = pr.dvec;
+  p.dq = static_cast<u16*>(pr.dq);
+  p.dk = static_cast<u16*>(pr.dk);
+  p.dv = static_cast<u16*>(pr.dv);
+  p.cu = pr.cu_seqlens;
+  p.B = pr.batch;
+  p.H = pr.heads;
+  p.N = pr.seqlen;
+  p.T = pr.total_tokens;
+  p.n_tiles = 0;
+  p.scale = pr.scale;
+  p.c = pr.scale * kLog2e;
+  return p;
+}
+
+template <int D, typename T>
+hipError_t launch_pre_t(const Problem& pr) {
+  const long long rows = (long long)pr.total_tokens * pr.heads;
+  constexpr int RPB = 256 / (D / 8);
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  if (pr.cu_seqlens)
+    hipLaunchKernelGGL((bwd_pre_kernel<D, T, true>), grid, dim3(256), 0, pr.stream,
+                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.dvec, pr.heads,
+                       pr.seqlen, pr.total_tokens, rows);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<D, T, false>), grid, dim3(256), 0, pr.stream,
+                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.dvec, pr.heads,
+                       pr.seqlen, pr.total_tokens, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_dkdv_t(const Problem& pr) {
+  BwdParams p = make_params(pr);
+  p.n_tiles = (pr.seqlen + kKvBK - 1) / kKvBK;
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>),
+                     dim3((unsigned)(p.n_tiles * pr.batch * pr.heads)), dim3(kKvThreads), 0, pr.stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_dq_t(const Problem& pr) {
+  BwdParams p = make_params(pr);
+  p.n_tiles = (pr.seqlen + kDqBR - 1) / kDqBR;
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, VARLEN>),
+                     dim3((unsigned)(p.n_tiles * pr.batch * pr.heads)), dim3(kDqThreads), 0, pr.stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre(const Problem& pr, bool fp32) {
+  if (fp32) return pr.head_dim == 64 ? launch_pre_t<64, float>(pr) : launch_pre_t<128, float>(pr);
+  return pr.head_dim == 64 ? launch_pre_t<64, u16>(pr) : launch_pre_t<128, u16>(pr);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const Problem& p) { FA_DISPATCH(launch_dkdv_t, p); }
+
+hipError_t launch_bwd_dq_bf16(const Problem& p) { FA_DISPATCH(launch_dq_t, p); }
+
+}  // namespace fa

@@ -1,0 +1,150 @@
+/*
+ * fa.h - exact IO-aware attention for AMD MI355X (gfx950): the C ABI of libfa.so.
+ *
+ * Computes exact scaled-dot-product attention, O = softmax(scale * Q K^T + mask) V,
+ * tile by tile with an online softmax, so the N x N score and probability matrices
+ * never reach device memory. The forward pass writes only O and the per-row
+ * logsumexp; the backward pass recomputes P block by block from it.
+ *
+ * Sources (web pages on FlashAttention), cited by title and section:
+ *  - "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness",
+ *    AI Atlas summary: "En pocas palabras" (same result as standard attention),
+ *    "Ideas clave" -> "Pensar en la E/S", "Tiling", "Softmax en línea",
+ *    "Recalcular en vez de guardar".
+ *  - "FlashAttention-2 (PT)", Systems analysis wiki: "Arquitetura técnica e
+ *    princípios de funcionamento" (fewer non-matmul FLOPs; parallelism across blocks
+ *    of one head; work split inside a block).
+ *  - "FlashAttention", aiunderstanding.org: "Plongée profonde", "Aperçu technique".
+ *  - "Flash Attention", docs.monostate.ai: "Con Sequence Packing" (packed batches).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except where noted is a DEVICE pointer owned by the caller.
+ *    The library never allocates, frees, or synchronises, and keeps no state between
+ *    calls. All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and is asynchronous: a device-side fault surfaces on the caller's next
+ *    synchronising call, not here.
+ *  - Layout: q, k, v, o, dout, dq, dk, dv are contiguous (batch, seqlen, heads,
+ *    head_dim), head_dim innermost. With cu_seqlens != NULL (a packed batch) they are
+ *    (total_tokens, heads, head_dim) and sequence b owns tokens
+ *    [cu_seqlens[b], cu_seqlens[b+1]); `seqlen` is then the longest sequence
+ *    (host-known; sizes the launch grid) and `batch` the number of sequences.
+ *  - lse: fp32 natural-log logsumexp of the scaled, masked scores of each query row,
+ *    (batch, heads, seqlen), or (heads, total_tokens) for a packed batch.
+ *  - dtype: FA_DTYPE_BF16 (tensors bf16, arithmetic fp32 with bf16 MFMA operands) or
+ *    FA_DTYPE_FP32 (tensors and all arithmetic fp32).
+ *  - head_dim in {64, 128}; seqlen >= 1; batch >= 1; heads >= 1; every tensor pointer
+ *    16-byte aligned. Queries and keys share one length (self-attention).
+ *  - causal != 0: query i sees key j iff j <= i, within its own sequence.
+ *  - Argument checks run on the host before any HIP call and return
+ *    FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_WORKSPACE without touching the
+ *    device. A failed launch returns FA_ERR_HIP.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad alignment, overflow */
+  FA_ERR_UNSUPPORTED = 2,  /* head_dim or dtype outside what the kernels are built for */
+  FA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than required        */
+  FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError != success)      */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
+
+/*
+ * Forward pass. Writes o (same dtype and layout as q) and lse (fp32).
+ * One workgroup per (sequence, head, query tile): parallel over the sequence, as in
+ * "FlashAttention-2 (PT)", "2. Paralelismo aprimorado". Each workgroup keeps its query
+ * tile in registers, streams key/value tiles through LDS, and carries the running row
+ * maximum and sum ("Softmax en línea"). Bitwise deterministic from run to run.
+ *
+ * total_tokens is read only when cu_seqlens != NULL; cu_seqlens is a device int32
+ * array of batch+1 non-decreasing prefix sums with cu_seqlens[0] = 0 and
+ * cu_seqlens[batch] = total_tokens, and no sequence longer than seqlen (the kernels
+ * do not check this: a violation is undefined behaviour).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int batch, int heads, int seqlen, int head_dim,
+           float softmax_scale, int causal,
+           const int32_t* cu_seqlens, int total_tokens,
+           int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: the fp32 row statistic
+ * D_i = sum_k dO_ik * O_ik, one per (head, query row), rounded up to 256 bytes.
+ * For a packed batch (varlen != 0) pass total_tokens; otherwise it is ignored.
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
+                              int varlen, int total_tokens);
+
+/*
+ * Backward pass for the loss gradient dout = dL/dO. Reads q, k, v, o, dout (as written
+ * by fa_fwd and the caller) and lse (from fa_fwd); writes dq, dk, dv in the dtype and
+ * layout of q. P is recomputed tile by tile from lse, never stored ("Recalcular en vez
+ * de guardar"). Three kernels run on `stream` (the stages below, in order):
+ *   1. D_i = rowsum(dO * O) for every query row, into the workspace;
+ *   2. one workgroup per (sequence, head, key tile) accumulating dK and dV on chip
+ *      while it walks the query tiles;
+ *   3. the dQ accumulation pass: one workgroup per (sequence, head, query tile)
+ *      accumulating dQ on chip while it walks the key tiles.
+ * No atomics: the result is bitwise deterministic from run to run.
+ * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned, owned by the caller; its contents on entry do not matter.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse,
+           void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int batch, int heads, int seqlen, int head_dim,
+           float softmax_scale, int causal,
+           const int32_t* cu_seqlens, int total_tokens,
+           int dtype, void* stream);
+
+/*
+ * The three stages of fa_bwd, callable on their own (same arguments, conventions and
+ * workspace as fa_bwd). fa_bwd_preprocess must complete before fa_bwd_dkdv and
+ * fa_bwd_dq start; those two only read the workspace and may run concurrently on
+ * different streams. Each enqueues exactly one kernel.
+ *
+ *  fa_bwd_preprocess: workspace <- D_i = sum_k dO_ik * O_ik (fp32, lse layout). D is
+ *    the row sum of P * dP, the term the softmax backward subtracts; computing it from
+ *    the stored O avoids touching P ("Recalcular en vez de guardar").
+ *  fa_bwd_dkdv: dk, dv. One workgroup per (sequence, head, key tile) accumulates dK and
+ *    dV on chip while walking the query tiles, recomputing P from lse.
+ *  fa_bwd_dq: dq. One workgroup per (sequence, head, query tile) accumulates dQ on chip
+ *    while walking the key tiles, recomputing P from lse.
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                      int batch, int heads, int seqlen, int head_dim,
+                      const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                int batch, int heads, int seqlen, int head_dim,
+                float softmax_scale, int causal,
+                const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const void* workspace, size_t workspace_bytes, void* dq,
+              int batch, int heads, int seqlen, int head_dim,
+              float softmax_scale, int causal,
+              const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports what include/fa.h declares, and
+rejects bad arguments with the documented codes before any HIP call (no GPU here)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_attention_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 1 << 20          # a 16-byte-aligned fake device address: never dereferenced on these paths
+MIS = A + 2          # misaligned
+
+
+def _lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libfa.so not built (python -m exact_io_aware_attention_amd.build)")
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess",
+                                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_strerror"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def _fwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, batch=1, heads=1, seqlen=16, head_dim=64, softmax_scale=0.125,
+                causal=0, cu_seqlens=None, total_tokens=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+def _bwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, workspace=A, workspace_bytes=1 << 30,
+                batch=1, heads=1, seqlen=16, head_dim=64, softmax_scale=0.125, causal=0, cu_seqlens=None,
+                total_tokens=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=0), fa.FA_ERR_INVALID_ARG),
+    (dict(heads=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(cu_seqlens=A, total_tokens=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=A + 1, total_tokens=4), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=1 << 20, heads=1 << 12, seqlen=1 << 12), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=A, total_tokens=0), fa.FA_OK),   # empty packed batch: nothing to launch
+])
+def test_fwd_argument_checks(kw, code):
+    _lib()
+    assert _fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=255), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=A + 16), fa.FA_ERR_WORKSPACE),
+    (dict(seqlen=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=A, total_tokens=0), fa.FA_OK),
+])
+def test_bwd_argument_checks(kw, code):
+    _lib()
+    assert _bwd(**kw) == code
+
+
+def test_stage_argument_checks():
+    _lib()
+    common = dict(batch=1, heads=2, seqlen=16, head_dim=64, cu_seqlens=None, total_tokens=0,
+                  dtype=fa.FA_DTYPE_BF16, stream=None)
+    ws = dict(workspace=A, workspace_bytes=1 << 20)
+    assert fa.fa_bwd_preprocess(o=None, dout=A, **ws, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, workspace=None, workspace_bytes=0, **common) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_preprocess(o=A, dout=A, **ws, **dict(common, head_dim=48)) == fa.FA_ERR_UNSUPPORTED
+    sc = dict(softmax_scale=0.125, causal=1)
+    assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=None, dv=A, **ws, **sc, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=A, dv=A, workspace=A, workspace_bytes=64,
+                          **sc, **common) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_dq(q=A, k=A, v=MIS, dout=A, lse=A, dq=A, **ws, **sc, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dq(q=A, k=A, v=A, dout=A, lse=A, dq=A, **ws, **dict(sc, causal=-1),
+                        **common) == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_size():
+    _lib()
+    assert fa.fa_bwd_workspace_bytes(4, 32, 4096, 128, 0, 0) == 4 * 32 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 3, 5, 64, 0, 0) == 256
+    assert fa.fa_bwd_workspace_bytes(7, 32, 2048, 128, 1, 16384) == 32 * 16384 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 80, 0, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64, 0, 0) == 0
+
+
+def test_strerror_covers_every_code():
+    _lib()
+    seen = set()
+    for code in range(5):
+        s = fa.fa_strerror(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in fa.fa_strerror(99)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "libfa.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        fa.load_library()
