@@ -91,10 +91,74 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------------
+// LDS transpose reads (ds_read_b64_tr_b16).
+// Within each group of 16 lanes, lane 4k + j supplies the address of an 8-byte run
+// (4 bf16) and output lane i receives element (i % 4) of the run supplied by lane
+// 4k + i / 4, for k = 0..3. When lane 4k + j points at row (r0 + k), columns
+// c0 + 4j .. c0 + 4j + 3 of a row-major tile, output lane i therefore holds column
+// c0 + i at rows r0 .. r0 + 3: a 16 x 4 block, transposed.
+// ---------------------------------------------------------------------------------------
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(__attribute__((address_space(3))) u16*)p);
+}
+
+// A operand (32 rows x 16 k-slots) of an MFMA whose k index runs along the rows of a
+// row-major LDS tile `t` (pitch in elements): A row m = tile column c0 + m, and the
+// 8 k-slots of lane group g are tile rows {r0 + 4g + 0..3, r0 + 8 + 4g + 0..3}, which
+// is exactly the order in which a 32x32 C register file (natural row order) holds
+// rows r0 .. r0 + 15 for lane group g in registers 8h .. 8h + 7 (h = r0 / 16 parity).
+__device__ __forceinline__ bf16x8 lds_tr_operand(const u16* t, int pitch, int r0, int c0, int lane) {
+  const int i = lane & 15;
+  const int G = lane >> 4;  // 16-lane group: (lane group g = G / 2, column half G % 2)
+  const u16* base = t + (r0 + 4 * (G >> 1) + (i >> 2)) * pitch + c0 + 16 * (G & 1) + 4 * (i & 3);
+  const i16x4 lo = ds_read_tr16(base);
+  const i16x4 hi = ds_read_tr16(base + 8 * pitch);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row (within a 32-row block) held by C register r of lane group g, natural order.
+__device__ __forceinline__ int crow_nat(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// ---------------------------------------------------------------------------------------
 // Global -> LDS tile staging. `src` points at row 0 of a matrix whose rows are
 // `stride` elements apart; rows [r0, r0 + ROWS) are staged and rows >= `len` are
 // zero-filled. All NT threads of the workgroup call these together.
 // ---------------------------------------------------------------------------------------
+
+// A tile's share of one thread, held in registers between the global load and the
+// LDS store (so the load of tile k+1 overlaps the math on tile k).
+template <int ROWS, int D, int NT>
+struct TileRegs {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int N = (ROWS * CPR + NT - 1) / NT;
+  u32x4 v[N];
+
+  __device__ __forceinline__ void load(const u16* __restrict__ src, int r0, int len, size_t stride, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if ((ROWS * CPR) % NT == 0 || c < ROWS * CPR)
+        if (r0 + row < len) v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * stride + col);
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(u16* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT;
+      if ((ROWS * CPR) % NT == 0 || c < ROWS * CPR)
+        *reinterpret_cast<u32x4*>(dst + (c / CPR) * PITCH + (c % CPR) * 8) = v[i];
+    }
+  }
+};
+
 
 // dst[ROWS][D + PAD], row-major, 16-byte chunks.
 template <int ROWS, int D, int PAD, int NT>

@@ -1,19 +1,29 @@
 // fa_fwd.hip - forward pass of exact attention, bf16 tensors, fp32 arithmetic (gfx950).
 //
-// One workgroup per (sequence, head, 128-query tile), so one head is spread over many
-// compute units ("FlashAttention-2 (PT)", "2. Paralelismo aprimorado"). Four waves; each
-// wave owns 32 query rows whose Q fragments stay in registers for the whole kernel.
-// Key/value tiles of 64 rows are staged through LDS ("Tiling" in the AI Atlas summary;
-// "Aperçu technique" on aiunderstanding.org) and each wave computes
+// One workgroup per (sequence, head, query tile), so one head is spread over many
+// compute units ("FlashAttention-2 (PT)", "2. Paralelismo aprimorado"). Four waves;
+// each wave owns QB blocks of 32 query rows whose Q fragments stay in registers for
+// the whole kernel. Key/value tiles of 64 rows are staged through LDS ("Tiling" in the
+// AI Atlas summary; "Aperçu technique" on aiunderstanding.org) and each wave computes
 //     S^T = K Q^T          (v_mfma_f32_32x32x16_bf16, fp32 accumulators)
 //     online softmax        (running max m and sum l per query row, "Softmax en línea")
 //     O^T += V^T P^T        (P converted to bf16 straight from the S^T registers)
 // Computing S transposed puts one query per MFMA output column, so each query's
 // softmax state sits in one lane and its mirror lane: a row reduction is in-register
 // work plus one lane swap, with no LDS round trip ("3. Divisão de trabalho otimizada
-// dentro do bloco"). The scale is folded into the exponent, c = scale * log2(e), and
-// the division by l happens once at the end ("1. Minimização de operações não
-// matriciais"). Only O and the logsumexp ever reach HBM.
+// dentro do bloco"). Non-matmul work is kept small ("1. Minimização de operações não
+// matriciais"): the scale is folded into the exponent, c = scale * log2(e); the
+// division by l happens once at the end; and the output is rescaled only when some
+// row's running maximum has grown by more than 2^8 since the last rescale (until then
+// the stale maximum keeps every exponent <= 2^8, so nothing overflows and O and l keep
+// one common reference, which is all exactness needs).
+//
+// Data movement: K and V tiles are copied row-major into LDS (16-byte writes); the
+// next tile's global loads are issued before the math on the current one and land in
+// the other half of a double-buffered LDS area, so each tile costs one barrier. K rows
+// feed the A operand of S^T directly; V^T is read with ds_read_b64_tr_b16, which
+// transposes 16 x 4 blocks on the way out of LDS. Row pitches are padded so both read
+// patterns hit distinct LDS banks.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -35,23 +45,114 @@ struct FwdParams {
 
 constexpr int kFwdWaves = 4;
 constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr int kFwdBR = 32 * kFwdWaves;  // queries per workgroup
-constexpr int kFwdBC = 64;              // keys per tile
-constexpr int kPadK = 8;                // bf16 padding per LDS row of K
-constexpr int kPadV = 8;                // bf16 padding per LDS row of V^T
+constexpr int kFwdBC = 64;        // keys per tile
+constexpr float kRescaleTau = 8.f;  // log2 growth of the row max tolerated before rescaling
 
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int BR = kFwdBR, BC = kFwdBC, NT = kFwdThreads;
-  constexpr int NB = D / 32;    // 32-wide head-dim blocks of O^T
-  constexpr int NS = D / 16;    // MFMA k-steps over the head dim
-  constexpr int NJ = BC / 32;   // 32-key blocks of S^T per tile
-  constexpr int NTK = BC / 16;  // MFMA k-steps over the keys of a tile
-  constexpr int KPITCH = D + kPadK;
-  constexpr int VPITCH = BC + kPadV;
+template <int D>
+struct FwdLds {
+  static constexpr int KP = D + 8;   // K row pitch (elements): rows land on distinct banks for b128
+  static constexpr int VP = D + 16;  // V row pitch: 4-row groups land on distinct banks for tr16
+  static constexpr int KSZ = kFwdBC * KP;
+  static constexpr int VSZ = kFwdBC * VP;
+  static constexpr int BUF = KSZ + VSZ;
+};
 
-  __shared__ __attribute__((aligned(16))) u16 Ks[BC * KPITCH];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * VPITCH];
+template <int D, int QB>
+struct FwdState {
+  static constexpr int NB = D / 32;
+  bf16x8 qf[QB][D / 16];
+  f32x16 oacc[QB][NB];
+  float m_run[QB];  // reference maximum of the raw scores q.k of this lane's query
+  float l_run[QB];  // this lane's share of sum_j exp2(c * (s_j - m_run))
+};
+
+// One key tile for one wave: S^T, softmax update, O^T += V^T P^T.
+template <int D, int QB, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
+                                         int wq0, int lane, float c) {
+  constexpr int NS = D / 16, NJ = kFwdBC / 32, NTK = kFwdBC / 16, NB = D / 32;
+  constexpr int KP = FwdLds<D>::KP, VP = FwdLds<D>::VP;
+  const int lr = lane & 31, g = lane >> 5;
+
+  f32x16 sacc[QB][NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int n = 0; n < QB; ++n) sacc[n][j] = f32x16{};
+    const u16* arow = Ks + (32 * j + lr) * KP + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = ld16(arow + 16 * s);
+#pragma unroll
+      for (int n = 0; n < QB; ++n) sacc[n][j] = mfma32(a, st.qf[n][s], sacc[n][j]);
+    }
+  }
+
+  bf16x8 pb[QB][NTK];
+#pragma unroll
+  for (int n = 0; n < QB; ++n) {
+    const int qi = wq0 + 32 * n + lr;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MASK) {
+          const int key = k0 + 32 * j + crow_nat(r, g);
+          const bool hide = key >= len || (CAUSAL && key > qi);
+          sacc[n][j][r] = hide ? -INFINITY : sacc[n][j][r];
+        }
+        mx = fmaxf(mx, sacc[n][j][r]);
+      }
+    }
+    mx = pair_max(mx);
+    const float m_new = fmaxf(st.m_run[n], mx);
+    // Rescale when this row's maximum grew by more than 2^tau (always on the first
+    // visible tile, where m_run is -inf); the decision is taken for the whole wave.
+    const bool grow = (m_new - st.m_run[n]) * c > kRescaleTau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_to = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2((st.m_run[n] - m_to) * c);
+      st.m_run[n] = m_new;
+      st.l_run[n] *= alpha;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) st.oacc[n][bb] *= alpha;
+    }
+    const float nb = st.m_run[n] == -INFINITY ? 0.f : -st.m_run[n] * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(sacc[n][j][r], c, nb));
+        sacc[n][j][r] = e;
+        ls += e;
+      }
+    }
+    st.l_run[n] += ls;
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) pb[n][t] = to_bf16x8(half_of(sacc[n][t >> 1], t & 1));
+  }
+
+  // O^T += V^T P^T: A row m of block bb is head-dim entry 32bb + m; the k-slots of lane
+  // group g at step t are keys 16t + 4g + {0..3, 8..11}, matching the P registers.
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) {
+      const bf16x8 a = lds_tr_operand(Vs, VP, 16 * t, 32 * bb, lane);
+#pragma unroll
+      for (int n = 0; n < QB; ++n) st.oacc[n][bb] = mfma32(a, pb[n][t], st.oacc[n][bb]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN, int QB>
+__global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int BR = 32 * QB * kFwdWaves, BC = kFwdBC, NT = kFwdThreads;
+  constexpr int NB = D / 32, NS = D / 16;
+  using L = FwdLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -80,112 +181,93 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const u16* __restrict__ Kg = p.k + base;
   const u16* __restrict__ Vg = p.v + base;
 
-  const int wq0 = q0 + 32 * w;  // first query row of this wave
-  const int qi = wq0 + lr;      // this lane's query row
-  const int wq_last = min(wq0 + 31, len - 1);
+  const int wq0 = q0 + 32 * QB * w;  // first query row of this wave
+  const int wq_last = min(wq0 + 32 * QB - 1, len - 1);
 
-  bf16x8 qf[NS];
+  FwdState<D, QB> st;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qf[s] = qi < len ? ld16(Qg + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
+  for (int n = 0; n < QB; ++n) {
+    const int qi = wq0 + 32 * n + lr;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      st.qf[n][s] = qi < len ? ld16(Qg + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) st.oacc[n][bb] = f32x16{};
+    st.m_run[n] = -INFINITY;
+    st.l_run[n] = 0.f;
+  }
 
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  float m_run = -INFINITY;  // running max of raw scores q.k for this query row
-  float l_run = 0.f;        // this lane's share of the running sum
-  f32x16 oacc[NB];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) oacc[bb] = f32x16{};
+  TileRegs<BC, D, NT> kr, vr;
+  kr.load(Kg, 0, len, stride, tid);
+  vr.load(Vg, 0, len, stride, tid);
+  kr.template store<L::KP>(lds, tid);
+  vr.template store<L::VP>(lds + L::KSZ, tid);
+  if (n_kt > 1) {
+    kr.load(Kg, BC, len, stride, tid);
+    vr.load(Vg, BC, len, stride, tid);
+  }
+  __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * BC;
-    if (kt > 0) __syncthreads();  // every wave is done reading the previous tile
-    stage_rows<BC, D, kPadK, NT>(Ks, Kg, k0, len, stride, tid);
-    stage_transposed<BC, D, kPadV, NT>(Vt, Vg, k0, len, stride, tid);
+    const u16* Ks = lds + (kt & 1) * L::BUF;
+    const u16* Vs = Ks + L::KSZ;
+    // wave-uniform: skip tiles that are entirely masked for this wave
+    if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
+      const bool full = k0 + BC <= len && (!CAUSAL || k0 + BC - 1 <= wq0);
+      if (full)
+        fwd_tile<D, QB, false, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, p.c);
+      else
+        fwd_tile<D, QB, true, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, p.c);
+    }
+    if (kt + 1 < n_kt) {
+      u16* nxt = lds + ((kt + 1) & 1) * L::BUF;
+      kr.template store<L::KP>(nxt, tid);
+      vr.template store<L::VP>(nxt + L::KSZ, tid);
+      if (kt + 2 < n_kt) {
+        kr.load(Kg, k0 + 2 * BC, len, stride, tid);
+        vr.load(Vg, k0 + 2 * BC, len, stride, tid);
+      }
+    }
     __syncthreads();
+  }
 
-    const bool active = wq0 < len && (!CAUSAL || k0 <= wq_last);
-    if (!active) continue;  // wave-uniform: this tile is entirely masked for the wave
-
-    // S^T = K Q^T for the 64 keys of the tile: register r of block j (lane group g)
-    // holds key k0 + 32j + crow_of_reg(r, g) against query qi.
-    f32x16 sacc[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      sacc[j] = f32x16{};
-      const u16* arow = Ks + (32 * j + perm_rows(lr)) * KPITCH + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) sacc[j] = mfma32(ld16(arow + 16 * s), qf[s], sacc[j]);
-    }
-
-    const bool need_mask = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > wq0);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (need_mask) {
-          const int key = k0 + 32 * j + crow_of_reg(r, g);
-          if (key >= len || (CAUSAL && key > qi)) sacc[j][r] = -INFINITY;
-        }
-        mx = fmaxf(mx, sacc[j][r]);
-      }
-    }
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no visible key yet
-    const float alpha = fast_exp2((m_run - m_use) * p.c);
-    const float nb = -m_use * p.c;
-    float ls = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(sacc[j][r], p.c, nb));
-        sacc[j][r] = e;
-        ls += e;
-      }
-    }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) oacc[bb] *= alpha;
-
-    bf16x8 pb[NTK];
-#pragma unroll
-    for (int t = 0; t < NTK; ++t) pb[t] = to_bf16x8(half_of(sacc[t >> 1], t & 1));
-
-    // O^T += V^T P^T: A row m of block bb is head-dim entry 32*bb + perm_cols(m); the
-    // 8 k-slots of lane group g at step t are keys 16t + 8g .. 16t + 8g + 7.
+  for (int n = 0; n < QB; ++n) {
+    const int qi = wq0 + 32 * n + lr;
+    const float l_tot = pair_sum(st.l_run[n]);
+    if (qi >= len) continue;
+    const float inv = 1.f / l_tot;
+    u16* __restrict__ Og = p.o + base + (size_t)qi * stride;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
-      const u16* arow = Vt + (32 * bb + perm_cols(lr)) * VPITCH + 8 * g;
+      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
 #pragma unroll
-      for (int t = 0; t < NTK; ++t) oacc[bb] = mfma32(ld16(arow + 16 * t), pb[t], oacc[bb]);
+      for (int a = 0; a < 4; ++a) {
+        const float x0 = st.oacc[n][bb][4 * a] * inv, x1 = st.oacc[n][bb][4 * a + 1] * inv;
+        const float x2 = st.oacc[n][bb][4 * a + 2] * inv, x3 = st.oacc[n][bb][4 * a + 3] * inv;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef float f32x4_ __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf16x4*>(Og + 32 * bb + 8 * a + 4 * g) =
+            __builtin_convertvector(f32x4_{x0, x1, x2, x3}, bf16x4);
+      }
     }
-  }
-
-  if (qi >= len) return;
-  const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
-  u16* __restrict__ Og = p.o + base + (size_t)qi * stride;
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    // lane group g holds head-dim entries 32bb + 16g + r, r = 0..15
-    const bf16x8 lo = to_bf16x8(half_of(oacc[bb], 0) * inv);
-    const bf16x8 hi = to_bf16x8(half_of(oacc[bb], 1) * inv);
-    *reinterpret_cast<bf16x8*>(Og + 32 * bb + 16 * g) = lo;
-    *reinterpret_cast<bf16x8*>(Og + 32 * bb + 16 * g + 8) = hi;
-  }
-  if (g == 0) {
-    const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
-    p.lse[li] = m_run * p.scale + logf(l_tot);
+    if (g == 0) {
+      const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
+      p.lse[li] = st.m_run[n] * p.scale + logf(l_tot);
+    }
   }
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_fwd_t(const Problem& pr) {
+  // Two query blocks per wave halve the LDS reads per MFMA; at head_dim 128 their
+  // accumulators no longer fit the register file, so one block is used there.
+  constexpr int QB = D == 64 ? 2 : 1;
+  constexpr int BR = 32 * QB * kFwdWaves;
   FwdParams p;
   p.q = static_cast<const u16*>(pr.q);
   p.k = static_cast<const u16*>(pr.k);
@@ -197,11 +279,11 @@ hipError_t launch_fwd_t(const Problem& pr) {
   p.H = pr.heads;
   p.N = pr.seqlen;
   p.T = pr.total_tokens;
-  p.n_qtiles = (pr.seqlen + kFwdBR - 1) / kFwdBR;
+  p.n_qtiles = (pr.seqlen + BR - 1) / BR;
   p.scale = pr.scale;
   p.c = pr.scale * kLog2e;
   const dim3 grid((unsigned)(p.n_qtiles * pr.batch * pr.heads));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(kFwdThreads), 0, pr.stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, QB>), grid, dim3(kFwdThreads), 0, pr.stream, p);
   return hipGetLastError();
 }
 
