@@ -110,25 +110,90 @@ constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
 constexpr int kKvBQ = 64;             // queries per tile
-constexpr int kPadRow = 8;
-constexpr int kPadT = 8;
+
+// One double-buffered half: Q and dO tiles (row-major; read both row-wise for S and
+// dP and through transpose reads for dK and dV), then LSE*log2(e) and D per query.
+template <int D>
+struct KvLds {
+  static constexpr int P = pitch_both<D>();
+  static constexpr int TSZ = kKvBQ * P;            // elements of one tile
+  static constexpr int STAT = 2 * TSZ;             // u16 offset of the fp32 statistics
+  static constexpr int BUF = 2 * TSZ + 4 * kKvBQ;  // + lse and D (2 x BQ floats)
+};
+
+template <int D>
+struct KvState {
+  static constexpr int NB = D / 32, NS = D / 16;
+  bf16x8 kf[NS], vf[NS];  // this lane's key and value rows as B operands
+  f32x16 dvT[NB], dkT[NB];
+};
+
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int lane, float c) {
+  constexpr int NB = D / 32, NS = D / 16, NA = kKvBQ / 32, NTQ = kKvBQ / 16;
+  constexpr int P = KvLds<D>::P;
+  const u16* Qs = buf;
+  const u16* dOs = buf + KvLds<D>::TSZ;
+  const float* lse_s = reinterpret_cast<const float*>(buf + KvLds<D>::STAT);
+  const float* dd_s = lse_s + kKvBQ;
+  const int lr = lane & 31, g = lane >> 5;
+
+  // S = Q K^T and dP = dO V^T, one key per column: register r of block a (lane group
+  // g) holds query q0 + 32a + crow_nat(r, g) against key kj.
+  f32x16 sacc[NA], dpacc[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    sacc[a] = f32x16{};
+    dpacc[a] = f32x16{};
+    const int off = (32 * a + lr) * P + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      sacc[a] = mfma32(ld16(Qs + off + 16 * s), st.kf[s], sacc[a]);
+      dpacc[a] = mfma32(ld16(dOs + off + 16 * s), st.vf[s], dpacc[a]);
+    }
+  }
+  // P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D)
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qrow = 32 * a + 8 * r4 + 4 * g;  // registers 4r4..4r4+3: queries qrow..qrow+3
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + qrow);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd_s + qrow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        float pv = fast_exp2(fmaf(sacc[a][r], c, -l4[e]));
+        if (MASK) pv = kj > q0 + qrow + e ? 0.f : pv;
+        sacc[a][r] = pv;
+        dpacc[a][r] = pv * (dpacc[a][r] - d4[e]);
+      }
+    }
+  }
+  bf16x8 pb[NTQ], dsb[NTQ];
+#pragma unroll
+  for (int t = 0; t < NTQ; ++t) {
+    pb[t] = to_bf16x8(half_of(sacc[t >> 1], t & 1));
+    dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
+  }
+  // dV^T += dO^T P and dK^T += Q^T dS: A row m of block bb is head-dim entry 32bb + m,
+  // read transposed from the row-major tiles; k-slots are queries 16t + 4g + {0..3, 8..11}.
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+    for (int t = 0; t < NTQ; ++t) {
+      st.dvT[bb] = mfma32(lds_tr_operand(dOs, P, 16 * t, 32 * bb, lane), pb[t], st.dvT[bb]);
+      st.dkT[bb] = mfma32(lds_tr_operand(Qs, P, 16 * t, 32 * bb, lane), dsb[t], st.dkT[bb]);
+    }
+  }
+}
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
   constexpr int BK = kKvBK, BQ = kKvBQ, NT = kKvThreads;
-  constexpr int NB = D / 32;    // 32-wide head-dim blocks of dK^T / dV^T
-  constexpr int NS = D / 16;    // k-steps over the head dim
-  constexpr int NA = BQ / 32;   // 32-query blocks of S per tile
-  constexpr int NTQ = BQ / 16;  // k-steps over the queries of a tile
-  constexpr int RP = D + kPadRow;
-  constexpr int TPITCH = BQ + kPadT;
-
-  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RP];
-  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RP];
-  __shared__ __attribute__((aligned(16))) u16 QT[D * TPITCH];
-  __shared__ __attribute__((aligned(16))) u16 dOT[D * TPITCH];
-  __shared__ __attribute__((aligned(16))) float lse_s[BQ];  // LSE * log2(e); +inf past the end
-  __shared__ __attribute__((aligned(16))) float dd_s[BQ];
+  constexpr int NB = D / 32, NS = D / 16;
+  using L = KvLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -158,86 +223,66 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int wk0 = k0 + 32 * w;  // first key of this wave
   const int kj = wk0 + lr;      // this lane's key
 
-  bf16x8 kf[NS], vf[NS];
+  KvState<D> st;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const size_t off = base + (size_t)kj * stride + 16 * s + 8 * g;
-    kf[s] = kj < len ? ld16(p.k + off) : zero_bf16x8();
-    vf[s] = kj < len ? ld16(p.v + off) : zero_bf16x8();
+    st.kf[s] = kj < len ? ld16(p.k + off) : zero_bf16x8();
+    st.vf[s] = kj < len ? ld16(p.v + off) : zero_bf16x8();
   }
-
-  f32x16 dvT[NB], dkT[NB];
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
-    dvT[bb] = f32x16{};
-    dkT[bb] = f32x16{};
+    st.dvT[bb] = f32x16{};
+    st.dkT[bb] = f32x16{};
   }
 
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
   const int n_qt = (len + BQ - 1) / BQ;
 
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
+  TileRegs<BQ, D, NT> qr, dr;
+  float lse_r = 0.f, dd_r = 0.f;
+  auto load_tile = [&](int qt) {
     const int q0 = qt * BQ;
-    if (qt > qt_begin) __syncthreads();
-    stage_rows<BQ, D, kPadRow, NT>(Qs, Qg, q0, len, stride, tid);
-    stage_rows<BQ, D, kPadRow, NT>(dOs, dOg, q0, len, stride, tid);
-    stage_transposed<BQ, D, kPadT, NT>(QT, Qg, q0, len, stride, tid);
-    stage_transposed<BQ, D, kPadT, NT>(dOT, dOg, q0, len, stride, tid);
+    qr.load(Qg, q0, len, stride, tid);
+    dr.load(dOg, q0, len, stride, tid);
     if (tid < BQ) {
       const int qq = q0 + tid;
-      lse_s[tid] = qq < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e : INFINITY;
-      dd_s[tid] = qq < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qq)] : 0.f;
+      // rows past the end get LSE = +inf, so their P (and dS) is exactly zero
+      lse_r = qq < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e : INFINITY;
+      dd_r = qq < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qq)] : 0.f;
+    }
+  };
+  auto store_tile = [&](u16* buf) {
+    qr.template store<L::P>(buf, tid);
+    dr.template store<L::P>(buf + L::TSZ, tid);
+    if (tid < BQ) {
+      float* st_ = reinterpret_cast<float*>(buf + L::STAT);
+      st_[tid] = lse_r;
+      st_[BQ + tid] = dd_r;
+    }
+  };
+
+  load_tile(qt_begin);
+  store_tile(lds);
+  if (qt_begin + 1 < n_qt) load_tile(qt_begin + 1);
+  __syncthreads();
+
+  for (int qt = qt_begin; qt < n_qt; ++qt) {
+    const int q0 = qt * BQ;
+    const int i = qt - qt_begin;
+    const u16* buf = lds + (i & 1) * L::BUF;
+    // wave-uniform: skip tiles whose queries all precede this wave's keys
+    if (wk0 < len && (!CAUSAL || q0 + BQ - 1 >= wk0)) {
+      if (CAUSAL && q0 < wk0 + 31)
+        dkdv_tile<D, true>(st, buf, q0, kj, lane, p.c);
+      else
+        dkdv_tile<D, false>(st, buf, q0, kj, lane, p.c);
+    }
+    if (qt + 1 < n_qt) {
+      store_tile(lds + ((i + 1) & 1) * L::BUF);
+      if (qt + 2 < n_qt) load_tile(qt + 2);
     }
     __syncthreads();
-
-    const bool active = wk0 < len && (!CAUSAL || q0 + BQ - 1 >= wk0);
-    if (!active) continue;
-
-    // S = Q K^T and dP = dO V^T with one key per column: register r of block a (lane
-    // group g) holds query q0 + 32a + crow_of_reg(r, g) against key kj.
-    f32x16 sacc[NA], dpacc[NA];
-#pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      sacc[a] = f32x16{};
-      dpacc[a] = f32x16{};
-      const int arow = (32 * a + perm_rows(lr)) * RP + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc[a] = mfma32(ld16(Qs + arow + 16 * s), kf[s], sacc[a]);
-        dpacc[a] = mfma32(ld16(dOs + arow + 16 * s), vf[s], dpacc[a]);
-      }
-    }
-
-    const bool need_mask = CAUSAL && q0 < wk0 + 31;
-#pragma unroll
-    for (int a = 0; a < NA; ++a) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = 32 * a + crow_of_reg(r, g);
-        float pv = fast_exp2(fmaf(sacc[a][r], p.c, -lse_s[qrow]));
-        if (need_mask && kj > q0 + qrow) pv = 0.f;
-        sacc[a][r] = pv;
-        dpacc[a][r] = pv * (dpacc[a][r] - dd_s[qrow]);
-      }
-    }
-
-    bf16x8 pb[NTQ], dsb[NTQ];
-#pragma unroll
-    for (int t = 0; t < NTQ; ++t) {
-      pb[t] = to_bf16x8(half_of(sacc[t >> 1], t & 1));
-      dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS: A row m of block bb is head-dim entry
-    // 32bb + perm_cols(m); k-slots of lane group g at step t are queries 16t + 8g + 0..7.
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int arow = (32 * bb + perm_cols(lr)) * TPITCH + 8 * g;
-#pragma unroll
-      for (int t = 0; t < NTQ; ++t) {
-        dvT[bb] = mfma32(ld16(dOT + arow + 16 * t), pb[t], dvT[bb]);
-        dkT[bb] = mfma32(ld16(QT + arow + 16 * t), dsb[t], dkT[bb]);
-      }
-    }
   }
 
   if (kj >= len) return;
@@ -245,10 +290,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
-    *reinterpret_cast<bf16x8*>(dKg + 32 * bb + 16 * g) = to_bf16x8(half_of(dkT[bb], 0) * p.scale);
-    *reinterpret_cast<bf16x8*>(dKg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dkT[bb], 1) * p.scale);
-    *reinterpret_cast<bf16x8*>(dVg + 32 * bb + 16 * g) = to_bf16x8(half_of(dvT[bb], 0));
-    *reinterpret_cast<bf16x8*>(dVg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dvT[bb], 1));
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
+      const int col = 32 * bb + 8 * a + 4 * g;
+      store_bf16x4(dKg + col, st.dkT[bb][4 * a] * p.scale, st.dkT[bb][4 * a + 1] * p.scale,
+                   st.dkT[bb][4 * a + 2] * p.scale, st.dkT[bb][4 * a + 3] * p.scale);
+      store_bf16x4(dVg + col, st.dvT[bb][4 * a], st.dvT[bb][4 * a + 1], st.dvT[bb][4 * a + 2],
+                   st.dvT[bb][4 * a + 3]);
+    }
   }
 }
 
@@ -259,16 +309,80 @@ constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqBR = 32 * kDqWaves;  // queries per workgroup
 constexpr int kDqBC = 64;             // keys per tile
 
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
-  constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
-  constexpr int NB = D / 32, NS = D / 16, NJ = BC / 32, NTK = BC / 16;
-  constexpr int RP = D + kPadRow;
-  constexpr int TPITCH = BC + kPadT;
+// One double-buffered half: K (read row-wise for S^T and transposed for dQ) and V
+// (row-wise for dP^T).
+template <int D>
+struct DqLds {
+  static constexpr int KP = pitch_both<D>();
+  static constexpr int VP = pitch_rows<D>();
+  static constexpr int KSZ = kDqBC * KP;
+  static constexpr int BUF = KSZ + kDqBC * VP;
+};
 
-  __shared__ __attribute__((aligned(16))) u16 Ks[BC * RP];
-  __shared__ __attribute__((aligned(16))) u16 Vs[BC * RP];
-  __shared__ __attribute__((aligned(16))) u16 KT[D * TPITCH];
+template <int D>
+struct DqState {
+  static constexpr int NB = D / 32, NS = D / 16;
+  bf16x8 qf[NS], dof[NS];  // this lane's query and output-gradient rows as B operands
+  f32x16 dqT[NB];
+  float lse2;  // LSE * log2(e) of this lane's query (+inf past the end)
+  float dd;    // D of this lane's query
+};
+
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, int len, int qi, int lane,
+                                        float c) {
+  constexpr int NB = D / 32, NS = D / 16, NJ = kDqBC / 32, NTK = kDqBC / 16;
+  constexpr int KP = DqLds<D>::KP, VP = DqLds<D>::VP;
+  const u16* Ks = buf;
+  const u16* Vs = buf + DqLds<D>::KSZ;
+  const int lr = lane & 31, g = lane >> 5;
+
+  // S^T = K Q^T and dP^T = V dO^T, one query per column: register r of block j (lane
+  // group g) holds key k0 + 32j + crow_nat(r, g) against query qi.
+  f32x16 sacc[NJ], dpacc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    sacc[j] = f32x16{};
+    dpacc[j] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      sacc[j] = mfma32(ld16(Ks + (32 * j + lr) * KP + 8 * g + 16 * s), st.qf[s], sacc[j]);
+      dpacc[j] = mfma32(ld16(Vs + (32 * j + lr) * VP + 8 * g + 16 * s), st.dof[s], dpacc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pv = fast_exp2(fmaf(sacc[j][r], c, -st.lse2));
+      if (MASK) {
+        const int key = k0 + 32 * j + crow_nat(r, g);
+        pv = (key >= len || (CAUSAL && key > qi)) ? 0.f : pv;
+      }
+      dpacc[j][r] = pv * (dpacc[j][r] - st.dd);
+    }
+  }
+  bf16x8 dsb[NTK];
+#pragma unroll
+  for (int t = 0; t < NTK; ++t) dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
+  // dQ^T += K^T dS^T: A row m of block bb is head-dim entry 32bb + m, read transposed
+  // from the row-major K tile; k-slots are keys 16t + 4g + {0..3, 8..11}.
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+    for (int t = 0; t < NTK; ++t)
+      st.dqT[bb] = mfma32(lds_tr_operand(Ks, KP, 16 * t, 32 * bb, lane), dsb[t], st.dqT[bb]);
+  }
+}
+
+// At head_dim 128 the per-lane state no longer fits the two-workgroup register budget
+// without spilling, so that variant runs one workgroup per compute unit.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(BwdParams p) {
+  constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
+  constexpr int NB = D / 32, NS = D / 16;
+  using L = DqLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -298,82 +412,64 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
   const int qi = wq0 + lr;
   const int wq_last = min(wq0 + 31, len - 1);
 
-  bf16x8 qf[NS], dof[NS];
+  DqState<D> st;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const size_t off = base + (size_t)qi * stride + 16 * s + 8 * g;
-    qf[s] = qi < len ? ld16(p.q + off) : zero_bf16x8();
-    dof[s] = qi < len ? ld16(p.dout + off) : zero_bf16x8();
+    st.qf[s] = qi < len ? ld16(p.q + off) : zero_bf16x8();
+    st.dof[s] = qi < len ? ld16(p.dout + off) : zero_bf16x8();
   }
-  const float lse_i = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] * kLog2e : INFINITY;
-  const float d_i = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
-
-  f32x16 dqT[NB];
+  st.lse2 = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] * kLog2e : INFINITY;
+  st.dd = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) dqT[bb] = f32x16{};
+  for (int bb = 0; bb < NB; ++bb) st.dqT[bb] = f32x16{};
 
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
+  TileRegs<BC, D, NT> kr, vr;
+  kr.load(Kg, 0, len, stride, tid);
+  vr.load(Vg, 0, len, stride, tid);
+  kr.template store<L::KP>(lds, tid);
+  vr.template store<L::VP>(lds + L::KSZ, tid);
+  if (n_kt > 1) {
+    kr.load(Kg, BC, len, stride, tid);
+    vr.load(Vg, BC, len, stride, tid);
+  }
+  __syncthreads();
+
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * BC;
-    if (kt > 0) __syncthreads();
-    stage_rows<BC, D, kPadRow, NT>(Ks, Kg, k0, len, stride, tid);
-    stage_rows<BC, D, kPadRow, NT>(Vs, Vg, k0, len, stride, tid);
-    stage_transposed<BC, D, kPadT, NT>(KT, Kg, k0, len, stride, tid);
+    const u16* buf = lds + (kt & 1) * L::BUF;
+    if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
+      const bool full = k0 + BC <= len && (!CAUSAL || k0 + BC - 1 <= wq0);
+      if (full)
+        dq_tile<D, false, CAUSAL>(st, buf, k0, len, qi, lane, p.c);
+      else
+        dq_tile<D, true, CAUSAL>(st, buf, k0, len, qi, lane, p.c);
+    }
+    if (kt + 1 < n_kt) {
+      u16* nxt = lds + ((kt + 1) & 1) * L::BUF;
+      kr.template store<L::KP>(nxt, tid);
+      vr.template store<L::VP>(nxt + L::KSZ, tid);
+      if (kt + 2 < n_kt) {
+        kr.load(Kg, k0 + 2 * BC, len, stride, tid);
+        vr.load(Vg, k0 + 2 * BC, len, stride, tid);
+      }
+    }
     __syncthreads();
-
-    const bool active = wq0 < len && (!CAUSAL || k0 <= wq_last);
-    if (!active) continue;
-
-    // S^T = K Q^T and dP^T = V dO^T with one query per column: register r of block j
-    // (lane group g) holds key k0 + 32j + crow_of_reg(r, g) against query qi.
-    f32x16 sacc[NJ], dpacc[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      sacc[j] = f32x16{};
-      dpacc[j] = f32x16{};
-      const int arow = (32 * j + perm_rows(lr)) * RP + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc[j] = mfma32(ld16(Ks + arow + 16 * s), qf[s], sacc[j]);
-        dpacc[j] = mfma32(ld16(Vs + arow + 16 * s), dof[s], dpacc[j]);
-      }
-    }
-
-    const bool need_mask = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > wq0);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sacc[j][r], p.c, -lse_i));
-        if (need_mask) {
-          const int key = k0 + 32 * j + crow_of_reg(r, g);
-          if (key >= len || (CAUSAL && key > qi)) pv = 0.f;
-        }
-        dpacc[j][r] = pv * (dpacc[j][r] - d_i);
-      }
-    }
-
-    bf16x8 dsb[NTK];
-#pragma unroll
-    for (int t = 0; t < NTK; ++t) dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
-    // dQ^T += K^T dS^T: A row m of block bb is head-dim entry 32bb + perm_cols(m);
-    // k-slots of lane group g at step t are keys 16t + 8g + 0..7.
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int arow = (32 * bb + perm_cols(lr)) * TPITCH + 8 * g;
-#pragma unroll
-      for (int t = 0; t < NTK; ++t) dqT[bb] = mfma32(ld16(KT + arow + 16 * t), dsb[t], dqT[bb]);
-    }
   }
 
   if (qi >= len) return;
   u16* __restrict__ dQg = p.dq + base + (size_t)qi * stride;
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
-    *reinterpret_cast<bf16x8*>(dQg + 32 * bb + 16 * g) = to_bf16x8(half_of(dqT[bb], 0) * p.scale);
-    *reinterpret_cast<bf16x8*>(dQg + 32 * bb + 16 * g + 8) = to_bf16x8(half_of(dqT[bb], 1) * p.scale);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int col = 32 * bb + 8 * a + 4 * g;
+      store_bf16x4(dQg + col, st.dqT[bb][4 * a] * p.scale, st.dqT[bb][4 * a + 1] * p.scale,
+                   st.dqT[bb][4 * a + 2] * p.scale, st.dqT[bb][4 * a + 3] * p.scale);
+    }
   }
 }
 

@@ -7,18 +7,13 @@
 //                real index sits in which slot is ours to choose, as long as A and B
 //                choose alike.
 //   C (32 x 32): lane l, register r holds row m = 8*(r/4) + 4*g + (r%4), column
-//                n = l % 32.
-// The kernels put one query (or one key) per C column, so per-row softmax state
-// lives in one lane and its mirror lane l ^ 32. Two row permutations make the C
-// registers of one product feed the next product's B operand without any data
-// movement:
-//   perm_rows(m): the tile row a lane loads into A row m, chosen so that register r of
-//                 C for lane group g holds row 16*(r/8) + 8*g + (r%8) of the 32-row block;
-//                 then registers 8h..8h+7 are rows 16h + 8g .. 16h + 8g + 7: eight
-//                 contiguous rows, exactly the k-slots of a B operand.
-//   perm_cols(m): the output column (head-dim index) loaded into A row m of the second
-//                 product, chosen so that lane group g ends up holding the 16 contiguous
-//                 head-dim entries 16g .. 16g + 15 of each 32-wide block (vector stores).
+//                n = l % 32 (crow_nat below).
+// The kernels put one query (or one key) per C column, so per-row state lives in one
+// lane and its mirror lane l ^ 32. The C registers of a first product (rows = keys or
+// queries of a tile) then serve directly as the B operand of a second product that
+// contracts over those rows: registers 8h .. 8h + 7 of lane group g hold rows
+// 16h + 4g + {0..3, 8..11}, and the matching A operand is fetched from the row-major
+// LDS tile with transpose reads (lds_tr_operand) in exactly that row order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,22 +35,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Swap bits 2 and 3 of a row index in [0, 32).
-__device__ __forceinline__ int perm_rows(int m) {
-  return (m & ~0xC) | ((m >> 2) & 1) << 3 | ((m >> 3) & 1) << 2;
-}
-
-// sigma(8j + 4g + i) = 16g + 4j + i for j in [0,4), g in [0,2), i in [0,4).
-__device__ __forceinline__ int perm_cols(int m) {
-  return (((m >> 2) & 1) << 4) | ((m >> 3) << 2) | (m & 3);
-}
-
-// Row (within a 32-row block) that C register r of lane group g holds after a product
-// whose A rows were loaded through perm_rows.
-__device__ __forceinline__ int crow_of_reg(int r, int g) {
-  return 16 * (r >> 3) + 8 * g + (r & 7);
-}
-
 __device__ __forceinline__ bf16x8 ld16(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -67,6 +46,12 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 // Eight fp32 -> eight bf16, round to nearest even.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x8& x) {
   return __builtin_convertvector(x, bf16x8);
+}
+
+// Four fp32 -> four bf16 (round to nearest even) stored as one 8-byte write.
+__device__ __forceinline__ void store_bf16x4(u16* dst, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{a, b, c, d}, bf16x4);
 }
 
 __device__ __forceinline__ f32x8 half_of(const f32x16& x, int h) {
@@ -120,6 +105,13 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const u16* t, int pitch, int r0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// LDS row pitches (in bf16 elements) that keep the two read patterns free of bank
+// conflicts: 16 consecutive rows read 16 bytes each at one column (A operands read
+// row-wise), or 4 consecutive rows read 32 bytes each (transpose reads).
+template <int D> constexpr int pitch_rows() { return D + 8; }
+template <int D> constexpr int pitch_tr() { return D + 16; }
+template <int D> constexpr int pitch_both() { return D == 64 ? D + 8 : D + 24; }
+
 // Row (within a 32-row block) held by C register r of lane group g, natural order.
 __device__ __forceinline__ int crow_nat(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
@@ -159,51 +151,5 @@ struct TileRegs {
   }
 };
 
-
-// dst[ROWS][D + PAD], row-major, 16-byte chunks.
-template <int ROWS, int D, int PAD, int NT>
-__device__ __forceinline__ void stage_rows(u16* dst, const u16* __restrict__ src, int r0, int len,
-                                           size_t stride, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int PITCH = D + PAD;
-#pragma unroll
-  for (int c = tid; c < ROWS * CPR; c += NT) {
-    const int row = c / CPR, col = (c % CPR) * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r0 + row < len) val = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * stride + col);
-    *reinterpret_cast<u32x4*>(dst + row * PITCH + col) = val;
-  }
-}
-
-// dst[D][ROWS + PAD]: the tile transposed (head-dim major), written as 8-byte runs of
-// four consecutive rows.
-template <int ROWS, int D, int PAD, int NT>
-__device__ __forceinline__ void stage_transposed(u16* dst, const u16* __restrict__ src, int r0, int len,
-                                                 size_t stride, int tid) {
-  constexpr int CG = D / 8;       // 8-column groups
-  constexpr int RG = ROWS / 4;    // 4-row groups
-  constexpr int PITCH = ROWS + PAD;
-#pragma unroll
-  for (int it = tid; it < RG * CG; it += NT) {
-    const int cg = it % CG, rg = it / CG;
-    u32x4 x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * rg + i;
-      x[i] = u32x4{0u, 0u, 0u, 0u};
-      if (row < len) x[i] = *reinterpret_cast<const u32x4*>(src + (size_t)row * stride + 8 * cg);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t a0 = (x[0][w] >> sh) & 0xffffu, a1 = (x[1][w] >> sh) & 0xffffu;
-      const uint32_t a2 = (x[2][w] >> sh) & 0xffffu, a3 = (x[3][w] >> sh) & 0xffffu;
-      uint2 packed;
-      packed.x = a0 | (a1 << 16);
-      packed.y = a2 | (a3 << 16);
-      *reinterpret_cast<uint2*>(dst + (8 * cg + e) * PITCH + 4 * rg) = packed;
-    }
-  }
-}
 
 }  // namespace fa

@@ -147,8 +147,10 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
   }
 }
 
+// Two query blocks per wave need the whole register file (one workgroup per compute
+// unit); so does the non-causal head_dim 128 variant, which spills at two.
 template <int D, bool CAUSAL, bool VARLEN, int QB>
-__global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 : 1) void fwd_bf16_kernel(FwdParams p) {
   constexpr int BR = 32 * QB * kFwdWaves, BC = kFwdBC, NT = kFwdThreads;
   constexpr int NB = D / 32, NS = D / 16;
   using L = FwdLds<D>;
