@@ -128,9 +128,17 @@ struct KvState {
   f32x16 dvT[NB], dkT[NB];
 };
 
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int lane, float c) {
-  constexpr int NB = D / 32, NS = D / 16, NA = kKvBQ / 32, NTQ = kKvBQ / 16;
+// One query tile for one wave, one 32-query block at a time (keeps the live score
+// registers to one block):
+//   S = Q K^T and dP = dO V^T with one key per column: register r of lane group g
+//   holds query q0 + 32a + crow_nat(r, g) against key kj;
+//   P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D);
+//   dV^T += dO^T P and dK^T += Q^T dS, whose A rows (head-dim entries) are read
+//   transposed from the row-major tiles with k-slots queries 16t + 4g + {0..3, 8..11}.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int len, bool mask,
+                                          int lane, float c) {
+  constexpr int NB = D / 32, NS = D / 16, NA = kKvBQ / 32;
   constexpr int P = KvLds<D>::P;
   const u16* Qs = buf;
   const u16* dOs = buf + KvLds<D>::TSZ;
@@ -138,52 +146,61 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
   const float* dd_s = lse_s + kKvBQ;
   const int lr = lane & 31, g = lane >> 5;
 
-  // S = Q K^T and dP = dO V^T, one key per column: register r of block a (lane group
-  // g) holds query q0 + 32a + crow_nat(r, g) against key kj.
-  f32x16 sacc[NA], dpacc[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    sacc[a] = f32x16{};
-    dpacc[a] = f32x16{};
-    const int off = (32 * a + lr) * P + 8 * g;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    {
+      const int off = (32 * a + lr) * P + 8 * g;
+      bf16x8 aq = ld16(Qs + off), ad = ld16(dOs + off);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sacc[a] = mfma32(ld16(Qs + off + 16 * s), st.kf[s], sacc[a]);
-      dpacc[a] = mfma32(ld16(dOs + off + 16 * s), st.vf[s], dpacc[a]);
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 nq = aq, nd = ad;
+        if (s + 1 < NS) {
+          nq = ld16(Qs + off + 16 * (s + 1));
+          nd = ld16(dOs + off + 16 * (s + 1));
+        }
+        sacc = mfma32(aq, st.kf[s], sacc);
+        dpacc = mfma32(ad, st.vf[s], dpacc);
+        aq = nq;
+        ad = nd;
+      }
     }
-  }
-  // P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D)
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int qrow = 32 * a + 8 * r4 + 4 * g;  // registers 4r4..4r4+3: queries qrow..qrow+3
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + qrow);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd_s + qrow);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        float pv = fast_exp2(fmaf(sacc[a][r], c, -l4[e]));
-        if (MASK) pv = kj > q0 + qrow + e ? 0.f : pv;
-        sacc[a][r] = pv;
-        dpacc[a][r] = pv * (dpacc[a][r] - d4[e]);
+      for (int e = 0; e < 4; ++e) sacc[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], c, -l4[e]));
+    }
+    if (mask) {  // wave-uniform: a diagonal or tail tile; hide keys after their query
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = q0 + 32 * a + crow_nat(r, g);
+        sacc[r] = (qq >= len || (CAUSAL && kj > qq)) ? 0.f : sacc[r];
       }
     }
-  }
-  bf16x8 pb[NTQ], dsb[NTQ];
 #pragma unroll
-  for (int t = 0; t < NTQ; ++t) {
-    pb[t] = to_bf16x8(half_of(sacc[t >> 1], t & 1));
-    dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
-  }
-  // dV^T += dO^T P and dK^T += Q^T dS: A row m of block bb is head-dim entry 32bb + m,
-  // read transposed from the row-major tiles; k-slots are queries 16t + 4g + {0..3, 8..11}.
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd_s + 32 * a + 8 * r4 + 4 * g);
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
+      for (int e = 0; e < 4; ++e) dpacc[4 * r4 + e] = sacc[4 * r4 + e] * (dpacc[4 * r4 + e] - d4[e]);
+    }
+    const bf16x8 pb0 = to_bf16x8(half_of(sacc, 0)), pb1 = to_bf16x8(half_of(sacc, 1));
+    const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
+    bf16x8 ao = lds_tr_operand(dOs, P, 32 * a, 0, lane), aq = lds_tr_operand(Qs, P, 32 * a, 0, lane);
 #pragma unroll
-    for (int t = 0; t < NTQ; ++t) {
-      st.dvT[bb] = mfma32(lds_tr_operand(dOs, P, 16 * t, 32 * bb, lane), pb[t], st.dvT[bb]);
-      st.dkT[bb] = mfma32(lds_tr_operand(Qs, P, 16 * t, 32 * bb, lane), dsb[t], st.dkT[bb]);
+    for (int i = 0; i < 2 * NB; ++i) {
+      const int bb = i >> 1, h = i & 1;
+      bf16x8 no = ao, nq = aq;
+      if (i + 1 < 2 * NB) {
+        const int bb1 = (i + 1) >> 1, h1 = (i + 1) & 1;
+        no = lds_tr_operand(dOs, P, 32 * a + 16 * h1, 32 * bb1, lane);
+        nq = lds_tr_operand(Qs, P, 32 * a + 16 * h1, 32 * bb1, lane);
+      }
+      mfma32_agpr(st.dvT[bb], ao, h ? pb1 : pb0);
+      mfma32_agpr(st.dkT[bb], aq, h ? ds1 : ds0);
+      ao = no;
+      aq = nq;
     }
   }
 }
@@ -193,7 +210,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   constexpr int BK = kKvBK, BQ = kKvBQ, NT = kKvThreads;
   constexpr int NB = D / 32, NS = D / 16;
   using L = KvLds<D>;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -239,52 +257,58 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
   const int n_qt = (len + BQ - 1) / BQ;
 
-  TileRegs<BQ, D, NT> qr, dr;
-  float lse_r = 0.f, dd_r = 0.f;
-  auto load_tile = [&](int qt) {
+  using TDma = TileDma<BQ, D, L::P, kKvWaves>;
+  float lse_r = 0.f, dd_r = 0.f;  // this thread's share of the next tile's statistics
+  auto issue = [&](int qt, u16* buf) {
     const int q0 = qt * BQ;
-    qr.load(Qg, q0, len, stride, tid);
-    dr.load(dOg, q0, len, stride, tid);
+    TDma::issue(buf, Qg, q0, len, stride, w, lane);
+    TDma::issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
     if (tid < BQ) {
-      const int qq = q0 + tid;
-      // rows past the end get LSE = +inf, so their P (and dS) is exactly zero
-      lse_r = qq < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e : INFINITY;
-      dd_r = qq < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qq)] : 0.f;
+      const int qq = min(q0 + tid, len - 1);  // rows past the end are masked in the tile
+      lse_r = p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e;
+      dd_r = p.dvec[stat_index<VARLEN>(p, b, h, start, qq)];
     }
   };
-  auto store_tile = [&](u16* buf) {
-    qr.template store<L::P>(buf, tid);
-    dr.template store<L::P>(buf + L::TSZ, tid);
+  auto finish = [&](u16* buf) {  // after the math: the statistics' loads have landed
     if (tid < BQ) {
       float* st_ = reinterpret_cast<float*>(buf + L::STAT);
       st_[tid] = lse_r;
       st_[BQ + tid] = dd_r;
     }
   };
-
-  load_tile(qt_begin);
-  store_tile(lds);
-  if (qt_begin + 1 < n_qt) load_tile(qt_begin + 1);
-  __syncthreads();
-
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
+  auto compute = [&](int qt, const u16* buf) {
     const int q0 = qt * BQ;
-    const int i = qt - qt_begin;
-    const u16* buf = lds + (i & 1) * L::BUF;
     // wave-uniform: skip tiles whose queries all precede this wave's keys
     if (wk0 < len && (!CAUSAL || q0 + BQ - 1 >= wk0)) {
-      if (CAUSAL && q0 < wk0 + 31)
-        dkdv_tile<D, true>(st, buf, q0, kj, lane, p.c);
-      else
-        dkdv_tile<D, false>(st, buf, q0, kj, lane, p.c);
+      const bool mask = q0 + BQ > len || (CAUSAL && q0 < wk0 + 31);
+      dkdv_tile<D, CAUSAL>(st, buf, q0, kj, len, mask, lane, p.c);
     }
-    if (qt + 1 < n_qt) {
-      store_tile(lds + ((i + 1) & 1) * L::BUF);
-      if (qt + 2 < n_qt) load_tile(qt + 2);
-    }
+  };
+  // Two LDS buffers in turn: the copy of the next query tile is in flight while the
+  // current one is used.
+  issue(qt_begin, buf0);
+  finish(buf0);
+  wait_vmem();
+  __syncthreads();
+  for (int qt = qt_begin; qt < n_qt; qt += 2) {
+    if (qt + 1 < n_qt) issue(qt + 1, buf1);
+    compute(qt, buf0);
+    if (qt + 1 < n_qt) finish(buf1);
+    wait_vmem();
+    __syncthreads();
+    if (qt + 1 >= n_qt) break;
+    if (qt + 2 < n_qt) issue(qt + 2, buf0);
+    compute(qt + 1, buf1);
+    if (qt + 2 < n_qt) finish(buf0);
+    wait_vmem();
     __syncthreads();
   }
 
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    agpr_acc_fence(st.dvT[bb]);
+    agpr_acc_fence(st.dkT[bb]);
+  }
   if (kj >= len) return;
   u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
   u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
@@ -328,9 +352,9 @@ struct DqState {
   float dd;    // D of this lane's query
 };
 
-template <int D, bool MASK, bool CAUSAL>
+template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, int len, int qi, int lane,
-                                        float c) {
+                                        float c, bool mask) {
   constexpr int NB = D / 32, NS = D / 16, NJ = kDqBC / 32, NTK = kDqBC / 16;
   constexpr int KP = DqLds<D>::KP, VP = DqLds<D>::VP;
   const u16* Ks = buf;
@@ -351,17 +375,23 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
     }
   }
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pv = fast_exp2(fmaf(sacc[j][r], c, -st.lse2));
-      if (MASK) {
+    for (int r = 0; r < 16; ++r) sacc[j][r] = fast_exp2(fmaf(sacc[j][r], c, -st.lse2));
+  if (mask) {  // wave-uniform: a diagonal or tail tile
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * j + crow_nat(r, g);
-        pv = (key >= len || (CAUSAL && key > qi)) ? 0.f : pv;
+        sacc[j][r] = (key >= len || (CAUSAL && key > qi)) ? 0.f : sacc[j][r];
       }
-      dpacc[j][r] = pv * (dpacc[j][r] - st.dd);
     }
   }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpacc[j][r] = sacc[j][r] * (dpacc[j][r] - st.dd);
   bf16x8 dsb[NTK];
 #pragma unroll
   for (int t = 0; t < NTK; ++t) dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
@@ -382,7 +412,8 @@ __global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kerne
   constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
   constexpr int NB = D / 32, NS = D / 16;
   using L = DqLds<D>;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -427,36 +458,31 @@ __global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kerne
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  TileRegs<BC, D, NT> kr, vr;
-  kr.load(Kg, 0, len, stride, tid);
-  vr.load(Vg, 0, len, stride, tid);
-  kr.template store<L::KP>(lds, tid);
-  vr.template store<L::VP>(lds + L::KSZ, tid);
-  if (n_kt > 1) {
-    kr.load(Kg, BC, len, stride, tid);
-    vr.load(Vg, BC, len, stride, tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
+  using KDma = TileDma<BC, D, L::KP, kDqWaves>;
+  using VDma = TileDma<BC, D, L::VP, kDqWaves>;
+  auto issue = [&](int kt, u16* buf) {
+    KDma::issue(buf, Kg, kt * BC, len, stride, w, lane);
+    VDma::issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
+  };
+  auto compute = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;
-    const u16* buf = lds + (kt & 1) * L::BUF;
     if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
-      const bool full = k0 + BC <= len && (!CAUSAL || k0 + BC - 1 <= wq0);
-      if (full)
-        dq_tile<D, false, CAUSAL>(st, buf, k0, len, qi, lane, p.c);
-      else
-        dq_tile<D, true, CAUSAL>(st, buf, k0, len, qi, lane, p.c);
+      const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);
+      dq_tile<D, CAUSAL>(st, buf, k0, len, qi, lane, p.c, mask);
     }
-    if (kt + 1 < n_kt) {
-      u16* nxt = lds + ((kt + 1) & 1) * L::BUF;
-      kr.template store<L::KP>(nxt, tid);
-      vr.template store<L::VP>(nxt + L::KSZ, tid);
-      if (kt + 2 < n_kt) {
-        kr.load(Kg, k0 + 2 * BC, len, stride, tid);
-        vr.load(Vg, k0 + 2 * BC, len, stride, tid);
-      }
-    }
+  };
+  issue(0, buf0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    if (kt + 1 < n_kt) issue(kt + 1, buf1);
+    compute(kt, buf0);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 >= n_kt) break;
+    if (kt + 2 < n_kt) issue(kt + 2, buf0);
+    compute(kt + 1, buf1);
+    wait_vmem();
     __syncthreads();
   }
 

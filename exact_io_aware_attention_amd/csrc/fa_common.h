@@ -35,6 +35,21 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc += a * b with the accumulator pinned to AGPRs. For accumulators that live across
+// a whole kernel loop and are touched only by MFMAs, this keeps them out of the VGPRs
+// the softmax arithmetic needs. The compiler cannot see hazards through inline asm, so
+// the two wait states a VALU-written A/B operand needs before an MFMA read are padded
+// here, and agpr_acc_fence must separate the last of these MFMAs from any VALU read
+// of the accumulator.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between an MFMA writing `acc` and VALU / v_accvgpr_read reads of it.
+__device__ __forceinline__ void agpr_acc_fence(f32x16& acc) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
+}
+
 __device__ __forceinline__ bf16x8 ld16(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -121,35 +136,36 @@ __device__ __forceinline__ int crow_nat(int r, int g) { return 8 * (r >> 2) + 4 
 // zero-filled. All NT threads of the workgroup call these together.
 // ---------------------------------------------------------------------------------------
 
-// A tile's share of one thread, held in registers between the global load and the
-// LDS store (so the load of tile k+1 overlaps the math on tile k).
-template <int ROWS, int D, int NT>
-struct TileRegs {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int N = (ROWS * CPR + NT - 1) / NT;
-  u32x4 v[N];
+// Global -> LDS copies of a tile with global_load_lds_dwordx4: each instruction moves
+// 64 lanes x 16 bytes straight into 1 KB of consecutive LDS, with no registers and no
+// LDS write instructions, and completes asynchronously (vmcnt). The LDS tile keeps its
+// padded row pitch: linear 16-byte chunk L of the tile is row L / CPP, chunk L % CPP
+// (CPP = PITCH / 8 chunks per row); lanes that land on a padding chunk copy the row's
+// first chunk there, which is never read. Rows at or past `len` are clamped to row
+// len - 1: the data is finite and every consumer masks those rows out.
+template <int ROWS, int D, int PITCH, int NWAVES>
+struct TileDma {
+  static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
+  static constexpr int CPP = PITCH / 8;
+  static constexpr int TOTAL = ROWS * CPP;
+  static constexpr int NINST = (TOTAL + 63) / 64;
 
-  __device__ __forceinline__ void load(const u16* __restrict__ src, int r0, int len, size_t stride, int tid) {
+  __device__ __forceinline__ static void issue(u16* dst, const u16* __restrict__ src, int r0, int len,
+                                               size_t stride, int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      v[i] = u32x4{0u, 0u, 0u, 0u};
-      if ((ROWS * CPR) % NT == 0 || c < ROWS * CPR)
-        if (r0 + row < len) v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * stride + col);
-    }
-  }
-
-  template <int PITCH>
-  __device__ __forceinline__ void store(u16* dst, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * NT;
-      if ((ROWS * CPR) % NT == 0 || c < ROWS * CPR)
-        *reinterpret_cast<u32x4*>(dst + (c / CPR) * PITCH + (c % CPR) * 8) = v[i];
+    for (int k = w; k < NINST; k += NWAVES) {  // wave-uniform
+      const int L = 64 * k + lane;
+      if (TOTAL % 64 == 0 || L < TOTAL) {
+        const int row = L / CPP, c = L % CPP;
+        const int grow = min(r0 + row, len - 1);
+        const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
+      }
     }
   }
 };
 
+// Wait for this wave's outstanding global loads (including LDS DMA) to land.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fa

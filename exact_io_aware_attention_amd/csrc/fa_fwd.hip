@@ -18,12 +18,12 @@
 // the stale maximum keeps every exponent <= 2^8, so nothing overflows and O and l keep
 // one common reference, which is all exactness needs).
 //
-// Data movement: K and V tiles are copied row-major into LDS (16-byte writes); the
-// next tile's global loads are issued before the math on the current one and land in
-// the other half of a double-buffered LDS area, so each tile costs one barrier. K rows
-// feed the A operand of S^T directly; V^T is read with ds_read_b64_tr_b16, which
-// transposes 16 x 4 blocks on the way out of LDS. Row pitches are padded so both read
-// patterns hit distinct LDS banks.
+// Data movement: K and V tiles are copied row-major into LDS by the global->LDS DMA
+// path (global_load_lds_dwordx4: no registers, no LDS write instructions); the copy of
+// the next tile runs while the current one is used, in the other of two LDS buffers,
+// so each tile costs one barrier. K rows feed the A operand of S^T directly; V^T is
+// read with ds_read_b64_tr_b16, which transposes 16 x 4 blocks on the way out of LDS.
+// Row pitches are padded so both read patterns hit distinct LDS banks.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -67,9 +67,9 @@ struct FwdState {
 };
 
 // One key tile for one wave: S^T, softmax update, O^T += V^T P^T.
-template <int D, int QB, bool MASK, bool CAUSAL>
+template <int D, int QB, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
-                                         int wq0, int lane, float c) {
+                                         int wq0, int lane, float c, bool mask) {
   constexpr int NS = D / 16, NJ = kFwdBC / 32, NTK = kFwdBC / 16, NB = D / 32;
   constexpr int KP = FwdLds<D>::KP, VP = FwdLds<D>::VP;
   const int lr = lane & 31, g = lane >> 5;
@@ -92,19 +92,22 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
-    float mx = -INFINITY;
+    if (mask) {  // wave-uniform: a diagonal or tail tile
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MASK) {
+        for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * j + crow_nat(r, g);
           const bool hide = key >= len || (CAUSAL && key > qi);
           sacc[n][j][r] = hide ? -INFINITY : sacc[n][j][r];
         }
-        mx = fmaxf(mx, sacc[n][j][r]);
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[n][j][r]);
     mx = pair_max(mx);
     const float m_new = fmaxf(st.m_run[n], mx);
     // Rescale when this row's maximum grew by more than 2^tau (always on the first
@@ -154,7 +157,8 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   constexpr int BR = 32 * QB * kFwdWaves, BC = kFwdBC, NT = kFwdThreads;
   constexpr int NB = D / 32, NS = D / 16;
   using L = FwdLds<D>;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
@@ -202,38 +206,33 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  TileRegs<BC, D, NT> kr, vr;
-  kr.load(Kg, 0, len, stride, tid);
-  vr.load(Vg, 0, len, stride, tid);
-  kr.template store<L::KP>(lds, tid);
-  vr.template store<L::VP>(lds + L::KSZ, tid);
-  if (n_kt > 1) {
-    kr.load(Kg, BC, len, stride, tid);
-    vr.load(Vg, BC, len, stride, tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
+  using KDma = TileDma<BC, D, L::KP, kFwdWaves>;
+  using VDma = TileDma<BC, D, L::VP, kFwdWaves>;
+  auto issue = [&](int kt, u16* buf) {
+    KDma::issue(buf, Kg, kt * BC, len, stride, w, lane);
+    VDma::issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
+  };
+  auto compute = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;
-    const u16* Ks = lds + (kt & 1) * L::BUF;
-    const u16* Vs = Ks + L::KSZ;
     // wave-uniform: skip tiles that are entirely masked for this wave
     if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
-      const bool full = k0 + BC <= len && (!CAUSAL || k0 + BC - 1 <= wq0);
-      if (full)
-        fwd_tile<D, QB, false, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, p.c);
-      else
-        fwd_tile<D, QB, true, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, p.c);
+      const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);
+      fwd_tile<D, QB, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
     }
-    if (kt + 1 < n_kt) {
-      u16* nxt = lds + ((kt + 1) & 1) * L::BUF;
-      kr.template store<L::KP>(nxt, tid);
-      vr.template store<L::VP>(nxt + L::KSZ, tid);
-      if (kt + 2 < n_kt) {
-        kr.load(Kg, k0 + 2 * BC, len, stride, tid);
-        vr.load(Vg, k0 + 2 * BC, len, stride, tid);
-      }
-    }
+  };
+  // Two LDS buffers in turn: the copy of tile kt+1 is in flight while tile kt is used.
+  issue(0, buf0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    if (kt + 1 < n_kt) issue(kt + 1, buf1);
+    compute(kt, buf0);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 >= n_kt) break;
+    if (kt + 2 < n_kt) issue(kt + 2, buf0);
+    compute(kt + 1, buf1);
+    wait_vmem();
     __syncthreads();
   }
 
