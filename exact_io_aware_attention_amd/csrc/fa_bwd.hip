@@ -216,11 +216,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
-  // Workgroup -> (sequence, head, key tile); under causal the first key tiles see the
-  // most queries, and they come first in launch order already.
-  const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;
+  // Workgroup -> (sequence, head, key tile), head-grouped per XCD (the head's Q and dO
+  // stay in L2); under causal the first key tiles see the most queries and come first.
+  int bh, kt;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, false, true, bh, kt);
   const int b = bh / p.H, h = bh % p.H;
   int start, len;
   if (VARLEN) {
@@ -257,12 +256,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int qt_begin = CAUSAL ? k0 / BQ : 0;
   const int n_qt = (len + BQ - 1) / BQ;
 
-  using TDma = TileDma<BQ, D, L::P, kKvWaves>;
+  TileDma<BQ, D, L::P, kKvWaves> tdma;
+  tdma.init(stride, w, lane);
   float lse_r = 0.f, dd_r = 0.f;  // this thread's share of the next tile's statistics
   auto issue = [&](int qt, u16* buf) {
     const int q0 = qt * BQ;
-    TDma::issue(buf, Qg, q0, len, stride, w, lane);
-    TDma::issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
+    tdma.issue(buf, Qg, q0, len, stride, w, lane);
+    tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
     if (tid < BQ) {
       const int qq = min(q0 + tid, len - 1);  // rows past the end are masked in the tile
       lse_r = p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e;
@@ -352,63 +352,70 @@ struct DqState {
   float dd;    // D of this lane's query
 };
 
+// One key tile for one wave, one 32-key block at a time (keeps the live score
+// registers to one block):
+//   S^T = K Q^T and dP^T = V dO^T with one query per column: register r of lane group
+//   g holds key k0 + 32j + crow_nat(r, g) against query qi;
+//   P = exp2(c S - LSE log2e), dS = P (dP - D);
+//   dQ^T += K^T dS^T, whose A rows (head-dim entries) are read transposed from the
+//   row-major K tile with k-slots keys 16t + 4g + {0..3, 8..11}.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, int len, int qi, int lane,
                                         float c, bool mask) {
-  constexpr int NB = D / 32, NS = D / 16, NJ = kDqBC / 32, NTK = kDqBC / 16;
+  constexpr int NB = D / 32, NS = D / 16, NJ = kDqBC / 32;
   constexpr int KP = DqLds<D>::KP, VP = DqLds<D>::VP;
   const u16* Ks = buf;
   const u16* Vs = buf + DqLds<D>::KSZ;
   const int lr = lane & 31, g = lane >> 5;
 
-  // S^T = K Q^T and dP^T = V dO^T, one query per column: register r of block j (lane
-  // group g) holds key k0 + 32j + crow_nat(r, g) against query qi.
-  f32x16 sacc[NJ], dpacc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    sacc[j] = f32x16{};
-    dpacc[j] = f32x16{};
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    {
+      const u16* kr = Ks + (32 * j + lr) * KP + 8 * g;
+      const u16* vr = Vs + (32 * j + lr) * VP + 8 * g;
+      bf16x8 ak = ld16(kr), av = ld16(vr);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sacc[j] = mfma32(ld16(Ks + (32 * j + lr) * KP + 8 * g + 16 * s), st.qf[s], sacc[j]);
-      dpacc[j] = mfma32(ld16(Vs + (32 * j + lr) * VP + 8 * g + 16 * s), st.dof[s], dpacc[j]);
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 nk = ak, nv = av;
+        if (s + 1 < NS) {
+          nk = ld16(kr + 16 * (s + 1));
+          nv = ld16(vr + 16 * (s + 1));
+        }
+        sacc = mfma32(ak, st.qf[s], sacc);
+        dpacc = mfma32(av, st.dof[s], dpacc);
+        ak = nk;
+        av = nv;
+      }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[j][r] = fast_exp2(fmaf(sacc[j][r], c, -st.lse2));
-  if (mask) {  // wave-uniform: a diagonal or tail tile
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, -st.lse2));
+    if (mask) {  // wave-uniform: a diagonal or tail tile
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * j + crow_nat(r, g);
-        sacc[j][r] = (key >= len || (CAUSAL && key > qi)) ? 0.f : sacc[j][r];
+        sacc[r] = (key >= len || (CAUSAL && key > qi)) ? 0.f : sacc[r];
       }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+    for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - st.dd);
+    const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
+    bf16x8 a = lds_tr_operand(Ks, KP, 32 * j, 0, lane);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dpacc[j][r] = sacc[j][r] * (dpacc[j][r] - st.dd);
-  bf16x8 dsb[NTK];
-#pragma unroll
-  for (int t = 0; t < NTK; ++t) dsb[t] = to_bf16x8(half_of(dpacc[t >> 1], t & 1));
-  // dQ^T += K^T dS^T: A row m of block bb is head-dim entry 32bb + m, read transposed
-  // from the row-major K tile; k-slots are keys 16t + 4g + {0..3, 8..11}.
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-#pragma unroll
-    for (int t = 0; t < NTK; ++t)
-      st.dqT[bb] = mfma32(lds_tr_operand(Ks, KP, 16 * t, 32 * bb, lane), dsb[t], st.dqT[bb]);
+    for (int i = 0; i < 2 * NB; ++i) {
+      const int bb = i >> 1, h = i & 1;
+      bf16x8 na = a;
+      if (i + 1 < 2 * NB) na = lds_tr_operand(Ks, KP, 32 * j + 16 * ((i + 1) & 1), 32 * ((i + 1) >> 1), lane);
+      st.dqT[bb] = mfma32(a, h ? ds1 : ds0, st.dqT[bb]);
+      a = na;
+    }
   }
 }
 
-// At head_dim 128 the per-lane state no longer fits the two-workgroup register budget
-// without spilling, so that variant runs one workgroup per compute unit.
+// Two workgroups per compute unit (two waves per SIMD) keep the matrix pipe busy while
+// the other wave waits on LDS or does its softmax arithmetic.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
   constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
   constexpr int NB = D / 32, NS = D / 16;
   using L = DqLds<D>;
@@ -418,10 +425,8 @@ __global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kerne
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
-  const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = p.n_tiles - 1 - qt;
+  int bh, qt;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, CAUSAL, false, bh, qt);
   const int b = bh / p.H, h = bh % p.H;
   int start, len;
   if (VARLEN) {
@@ -458,11 +463,13 @@ __global__ __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) void bwd_dq_bf16_kerne
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  using KDma = TileDma<BC, D, L::KP, kDqWaves>;
-  using VDma = TileDma<BC, D, L::VP, kDqWaves>;
+  TileDma<BC, D, L::KP, kDqWaves> kdma;
+  TileDma<BC, D, L::VP, kDqWaves> vdma;
+  kdma.init(stride, w, lane);
+  vdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
-    KDma::issue(buf, Kg, kt * BC, len, stride, w, lane);
-    VDma::issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
+    kdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
+    vdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
   };
   auto compute = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;

@@ -50,6 +50,29 @@ __device__ __forceinline__ void agpr_acc_fence(f32x16& acc) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
 }
 
+// Workgroup index -> (sequence*head index bh, tile index t) for a grid of BH x NT
+// workgroups. Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on
+// XCD i % 8) and each XCD has its own L2.
+//  - tile-major (xcd_group = false): workgroup L is head L % BH, tile L / BH. When BH
+//    is a multiple of 8, every tile of a head still lands on one XCD, and under causal
+//    masking (rev = true: tile order reversed) the longest rows of all heads are issued
+//    first, which balances the causal work best.
+//  - head-grouped (xcd_group = true, BH a multiple of 8): the k-th workgroup an XCD
+//    receives is head (k / NT) * 8 + xcd, tile k % NT, so an XCD works through all tiles
+//    of one head before the next and the head's operands stay in that XCD's L2.
+__device__ __forceinline__ void xcd_tile_map(int L, int BH, int NT, bool rev, bool xcd_group, int& bh, int& t) {
+  constexpr int kXcds = 8;
+  if (xcd_group && BH % kXcds == 0) {
+    const int xcd = L % kXcds, k = L / kXcds;
+    bh = (k / NT) * kXcds + xcd;
+    t = k % NT;
+  } else {
+    bh = L % BH;
+    t = L / BH;
+  }
+  if (rev) t = NT - 1 - t;
+}
+
 __device__ __forceinline__ bf16x8 ld16(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -120,11 +143,14 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const u16* t, int pitch, int r0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// LDS row pitches (in bf16 elements) that keep the two read patterns free of bank
-// conflicts: 16 consecutive rows read 16 bytes each at one column (A operands read
-// row-wise), or 4 consecutive rows read 32 bytes each (transpose reads).
+// LDS row pitches (in bf16 elements). Row-wise A-operand reads (ds_read_b128) are
+// serviced 16 lanes at a time, 16 consecutive rows x 16 bytes: a pitch of 4 (mod 64)
+// dwords puts them on distinct banks. Transpose reads (ds_read_b64_tr_b16) are serviced
+// 32 lanes at a time, 4 consecutive rows x 64 bytes: a pitch of 16 (mod 64) dwords
+// does. (Measured with the LDS bank-conflict counter.) A tile read both ways cannot
+// satisfy both and uses pitch_both, which favours the row-wise reads.
 template <int D> constexpr int pitch_rows() { return D + 8; }
-template <int D> constexpr int pitch_tr() { return D + 16; }
+template <int D> constexpr int pitch_tr() { return D + 32; }
 template <int D> constexpr int pitch_both() { return D == 64 ? D + 8 : D + 24; }
 
 // Row (within a 32-row block) held by C register r of lane group g, natural order.
@@ -149,19 +175,42 @@ struct TileDma {
   static constexpr int CPP = PITCH / 8;
   static constexpr int TOTAL = ROWS * CPP;
   static constexpr int NINST = (TOTAL + 63) / 64;
+  static constexpr int PER_WAVE = (NINST + NWAVES - 1) / NWAVES;
 
-  __device__ __forceinline__ static void issue(u16* dst, const u16* __restrict__ src, int r0, int len,
-                                               size_t stride, int w, int lane) {
+  __device__ __forceinline__ void init(size_t, int, int) {}
+
+  // Copy rows [r0, r0 + ROWS) of `src` into `dst`. The body is compiled for the device
+  // only: hipcc's host pass otherwise drops (without a diagnostic) the launch stubs of
+  // kernels that inline this control flow.
+  __device__ __forceinline__ void issue(u16* dst, const u16* __restrict__ src, int r0, int len, size_t stride,
+                                        int w, int lane) const {
+#if __HIP_DEVICE_COMPILE__
+    if (r0 + ROWS <= len) {  // wave-uniform: a full tile, no clamping
+      const u16* base = src + (size_t)r0 * stride;
 #pragma unroll
-    for (int k = w; k < NINST; k += NWAVES) {  // wave-uniform
-      const int L = 64 * k + lane;
-      if (TOTAL % 64 == 0 || L < TOTAL) {
-        const int row = L / CPP, c = L % CPP;
-        const int grow = min(r0 + row, len - 1);
-        const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int k = w + i * NWAVES;
+        const int L = 64 * k + lane;
+        if (k < NINST && (TOTAL % 64 == 0 || L < TOTAL)) {
+          const int row = L / CPP, c = L % CPP;
+          __builtin_amdgcn_global_load_lds(base + (uint32_t)(row * stride) + (c < D / 8 ? 8 * c : 0),
+                                           (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int k = w + i * NWAVES;
+        const int L = 64 * k + lane;
+        if (k < NINST && (TOTAL % 64 == 0 || L < TOTAL)) {
+          const int row = L / CPP, c = L % CPP;
+          const int grow = min(r0 + row, len - 1);
+          const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
+          __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
+        }
       }
     }
+#endif
   }
 };
 

@@ -50,8 +50,8 @@ constexpr float kRescaleTau = 8.f;  // log2 growth of the row max tolerated befo
 
 template <int D>
 struct FwdLds {
-  static constexpr int KP = D + 8;   // K row pitch (elements): rows land on distinct banks for b128
-  static constexpr int VP = D + 16;  // V row pitch: 4-row groups land on distinct banks for tr16
+  static constexpr int KP = pitch_rows<D>();  // K: read row-wise (A operand of S^T)
+  static constexpr int VP = pitch_tr<D>();    // V: read with transpose reads (A of O^T)
   static constexpr int KSZ = kFwdBC * KP;
   static constexpr int VSZ = kFwdBC * VP;
   static constexpr int BUF = KSZ + VSZ;
@@ -163,12 +163,10 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
-  // Workgroup -> (sequence, head, query tile). Causal tiles near the end of a sequence
-  // have the most keys to visit, so they are issued first.
-  const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
+  // Workgroup -> (sequence, head, query tile), tile-major; causal tiles near the end of
+  // a sequence have the most keys to visit, so they are issued first.
+  int bh, qt;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_qtiles, CAUSAL, false, bh, qt);
   const int b = bh / p.H, h = bh % p.H;
   int start, len;
   if (VARLEN) {
@@ -206,11 +204,13 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  using KDma = TileDma<BC, D, L::KP, kFwdWaves>;
-  using VDma = TileDma<BC, D, L::VP, kFwdWaves>;
+  TileDma<BC, D, L::KP, kFwdWaves> kdma;
+  TileDma<BC, D, L::VP, kFwdWaves> vdma;
+  kdma.init(stride, w, lane);
+  vdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
-    KDma::issue(buf, Kg, kt * BC, len, stride, w, lane);
-    VDma::issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
+    kdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
+    vdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
   };
   auto compute = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;

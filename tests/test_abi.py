@@ -44,6 +44,15 @@ def test_library_exports_every_declared_symbol():
         assert getattr(lib, name) is not None
 
 
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel launch stub is defined (a host-pass miscompile once left them
+    undefined, which only shows up as a load failure on the GPU machine)."""
+    _lib()
+    out = subprocess.run(["nm", "-D", fa.library_path()], capture_output=True, text=True, check=True).stdout
+    missing = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
+    assert missing == []
+
+
 def _fwd(**kw):
     args = dict(q=A, k=A, v=A, o=A, lse=A, batch=1, heads=1, seqlen=16, head_dim=64, softmax_scale=0.125,
                 causal=0, cu_seqlens=None, total_tokens=0, dtype=fa.FA_DTYPE_BF16, stream=None)
