@@ -165,6 +165,11 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
         ad = nd;
       }
     }
+    // The transposed A operands of dV += P^T dO do not depend on the softmax arithmetic:
+    // fetch them now, so that their LDS latency hides under it.
+    bf16x8 aot[2 * NB];
+#pragma unroll
+    for (int i = 0; i < 2 * NB; ++i) aot[i] = lds_tr_operand(dOs, P, 32 * a + 16 * (i & 1), 32 * (i >> 1), lane);
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int qrow = 32 * a + 8 * r4 + 4 * g;  // registers 4r4..4r4+3: queries qrow..qrow+3
@@ -186,22 +191,16 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
       for (int e = 0; e < 4; ++e) dpacc[4 * r4 + e] = sacc[4 * r4 + e] * (dpacc[4 * r4 + e] - d4[e]);
     }
     const bf16x8 pb0 = to_bf16x8(half_of(sacc, 0)), pb1 = to_bf16x8(half_of(sacc, 1));
-    const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
-    bf16x8 ao = lds_tr_operand(dOs, P, 32 * a, 0, lane), aq = lds_tr_operand(Qs, P, 32 * a, 0, lane);
+    // dV += P^T dO, fetching the transposed Q operands of dK += dS^T Q meanwhile.
+    bf16x8 aqt[2 * NB];
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
-      const int bb = i >> 1, h = i & 1;
-      bf16x8 no = ao, nq = aq;
-      if (i + 1 < 2 * NB) {
-        const int bb1 = (i + 1) >> 1, h1 = (i + 1) & 1;
-        no = lds_tr_operand(dOs, P, 32 * a + 16 * h1, 32 * bb1, lane);
-        nq = lds_tr_operand(Qs, P, 32 * a + 16 * h1, 32 * bb1, lane);
-      }
-      mfma32_agpr(st.dvT[bb], ao, h ? pb1 : pb0);
-      mfma32_agpr(st.dkT[bb], aq, h ? ds1 : ds0);
-      ao = no;
-      aq = nq;
+      aqt[i] = lds_tr_operand(Qs, P, 32 * a + 16 * (i & 1), 32 * (i >> 1), lane);
+      st.dvT[i >> 1] = mfma32(aot[i], (i & 1) ? pb1 : pb0, st.dvT[i >> 1]);
     }
+    const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
+#pragma unroll
+    for (int i = 0; i < 2 * NB; ++i) st.dkT[i >> 1] = mfma32(aqt[i], (i & 1) ? ds1 : ds0, st.dkT[i >> 1]);
   }
 }
 
@@ -304,11 +303,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     __syncthreads();
   }
 
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    agpr_acc_fence(st.dvT[bb]);
-    agpr_acc_fence(st.dkT[bb]);
-  }
   if (kj >= len) return;
   u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
   u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;

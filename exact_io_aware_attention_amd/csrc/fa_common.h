@@ -35,21 +35,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// acc += a * b with the accumulator pinned to AGPRs. For accumulators that live across
-// a whole kernel loop and are touched only by MFMAs, this keeps them out of the VGPRs
-// the softmax arithmetic needs. The compiler cannot see hazards through inline asm, so
-// the two wait states a VALU-written A/B operand needs before an MFMA read are padded
-// here, and agpr_acc_fence must separate the last of these MFMAs from any VALU read
-// of the accumulator.
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Wait states between an MFMA writing `acc` and VALU / v_accvgpr_read reads of it.
-__device__ __forceinline__ void agpr_acc_fence(f32x16& acc) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
-}
-
 // Workgroup index -> (sequence*head index bh, tile index t) for a grid of BH x NT
 // workgroups. Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on
 // XCD i % 8) and each XCD has its own L2.
