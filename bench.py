@@ -34,6 +34,32 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s, bf16 d=128 N=4096 causal; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
+
+# HBM traffic per launch of a kernel, from two rocprofv3 --pmc passes over this script
+# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) on the named workload, each scaled by
+# the ratio that the same counter shows for a copy kernel of known size run in the same
+# process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
+# the value they had when the counters were taken; otherwise null.
+TRAFFIC = {}
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload: str, kernel: str):
+    t = TRAFFIC.get((workload, kernel))
+    if t is None or t["sources_sha256"] != sources_sha256():
+        return None
+    return t
 
 
 def log(*a):
@@ -89,6 +115,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before the warmup, run a plain fp32 copy kernel (y = -x) over this many MiB, "
+                         "three times, as the known-size reference for HBM byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the attention path has no "
@@ -144,6 +173,16 @@ def main(argv=None) -> int:
                            dt_code, sp), "fa_bwd_dq")
 
     kernels = [("fwd", k_fwd), ("bwd_preprocess", k_pre), ("bwd_dkdv", k_dkdv), ("bwd_dq", k_dq)]
+    if a.calibrate_copy_mib > 0:
+        n = a.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # reads and writes calibrate_copy_mib MiB each
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, {a.calibrate_copy_mib} MiB read + {a.calibrate_copy_mib} MiB written "
+            f"per launch, 3 launches")
+        del src, dst
     log(f"bench: warmup {a.warmup}")
     for _ in range(a.warmup):
         for _, fn in kernels:
@@ -173,6 +212,7 @@ def main(argv=None) -> int:
     value = (fwd_fl + bwd_fl) / (step_ms * 1e-3) / 1e12
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
     achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
+    tr = traffic_for(w.name, dom)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -205,9 +245,15 @@ def main(argv=None) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if tr is None else tr["bytes"],
         },
     }
+    if tr is not None:
+        out["roofline"]["traffic_detail"] = {
+            "hbm_bytes_per_launch": tr["bytes"], "fetch_kib": tr["fetch_kib"], "write_kib": tr["write_kib"],
+            "fetch_factor": tr["fetch_factor"], "write_factor": tr["write_factor"],
+            "achieved_hbm_gbs": round(tr["bytes"] / (per[dom] * 1e-3) / 1e9, 1),
+            "profile": tr["profile"]}
     if a.cpu_budget > 0 and w.varlen is False:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)

@@ -213,7 +213,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
   // Workgroup -> (sequence, head, key tile), head-grouped per XCD (the head's Q and dO
   // stay in L2); under causal the first key tiles see the most queries and come first.
@@ -417,7 +418,8 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
   int bh, qt;
   xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, CAUSAL, false, bh, qt);

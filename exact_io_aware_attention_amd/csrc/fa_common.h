@@ -159,40 +159,51 @@ struct TileDma {
   static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
   static constexpr int CPP = PITCH / 8;
   static constexpr int TOTAL = ROWS * CPP;
-  static constexpr int NINST = (TOTAL + 63) / 64;
+  static_assert(TOTAL % 64 == 0, "a tile must be a whole number of 64-chunk copies");
+  static constexpr int NINST = TOTAL / 64;
   static constexpr int PER_WAVE = (NINST + NWAVES - 1) / NWAVES;
 
-  __device__ __forceinline__ void init(size_t, int, int) {}
+  // Byte offset, from the tile's first row in global memory, of the chunk this lane
+  // copies in each of its instructions. It does not depend on the tile, so it is
+  // computed once. Wave w issues copies w, w + NWAVES, ...; a wave with one copy
+  // fewer repeats the last one (same bytes to the same place), which keeps the issue
+  // free of branches.
+  uint32_t off[PER_WAVE];
 
-  // Copy rows [r0, r0 + ROWS) of `src` into `dst`. The body is compiled for the device
-  // only: hipcc's host pass otherwise drops (without a diagnostic) the launch stubs of
-  // kernels that inline this control flow.
+  __device__ __forceinline__ static int copy_index(int w, int i) { return min(w + i * NWAVES, NINST - 1); }
+
+  __device__ __forceinline__ void init(size_t stride, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int L = 64 * copy_index(w, i) + lane;
+      const int row = L / CPP, c = L % CPP;
+      off[i] = (uint32_t)(((size_t)row * stride + (c < D / 8 ? 8 * c : 0)) * sizeof(u16));
+    }
+  }
+
+  // Copy rows [r0, r0 + ROWS) of `src` into `dst` (w: the wave index, uniform). Rows at
+  // or past `len` are copies of row len - 1 (the consumer masks them). The body is
+  // compiled for the device only: hipcc's host pass otherwise drops (without a
+  // diagnostic) the launch stubs of kernels that inline this control flow.
   __device__ __forceinline__ void issue(u16* dst, const u16* __restrict__ src, int r0, int len, size_t stride,
                                         int w, int lane) const {
 #if __HIP_DEVICE_COMPILE__
-    if (r0 + ROWS <= len) {  // wave-uniform: a full tile, no clamping
-      const u16* base = src + (size_t)r0 * stride;
+    if (r0 + ROWS <= len) {  // wave-uniform: a full tile
+      const char* base = reinterpret_cast<const char*>(src + (size_t)r0 * stride);
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        const int k = w + i * NWAVES;
-        const int L = 64 * k + lane;
-        if (k < NINST && (TOTAL % 64 == 0 || L < TOTAL)) {
-          const int row = L / CPP, c = L % CPP;
-          __builtin_amdgcn_global_load_lds(base + (uint32_t)(row * stride) + (c < D / 8 ? 8 * c : 0),
-                                           (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
-        }
-      }
+      for (int i = 0; i < PER_WAVE; ++i)
+        __builtin_amdgcn_global_load_lds(base + off[i],
+                                         (__attribute__((address_space(3))) void*)(dst + 512 * copy_index(w, i)),
+                                         16, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        const int k = w + i * NWAVES;
+        const int k = copy_index(w, i);
         const int L = 64 * k + lane;
-        if (k < NINST && (TOTAL % 64 == 0 || L < TOTAL)) {
-          const int row = L / CPP, c = L % CPP;
-          const int grow = min(r0 + row, len - 1);
-          const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
-          __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
-        }
+        const int row = L / CPP, c = L % CPP;
+        const int grow = min(r0 + row, len - 1);
+        const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
       }
     }
 #endif

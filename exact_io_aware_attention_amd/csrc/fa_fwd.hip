@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
 
   // Workgroup -> (sequence, head, query tile), tile-major; causal tiles near the end of
   // a sequence have the most keys to visit, so they are issued first.
