@@ -34,6 +34,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file additions. The forward kernel runs one wave per SIMD with its output
+# accumulators pinned in AGPRs by inline asm; every other MFMA there must use the VGPR
+# form, so the score accumulators stay where the softmax arithmetic reads them.
+FILE_FLAGS = {
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -65,7 +73,8 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o],
+                          verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
     tmp = LIB_PATH + ".tmp"

@@ -35,6 +35,22 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// O^T += A B on accumulators held in AGPRs. Under a 512-register budget (one wave per
+// SIMD) the output accumulators live in AGPRs for a whole kernel and are touched only by
+// these MFMAs, while everything else (compiled with VGPR-form MFMAs) stays in VGPRs. The
+// compiler cannot see hazards through inline asm, so the two wait states that a
+// VALU-written A/B operand needs before an MFMA read are padded here, and
+// agpr_acc_fence must separate the last of these MFMAs from any VALU or v_accvgpr_read
+// access to the accumulator.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between an MFMA writing `acc` and VALU / v_accvgpr_read reads of it.
+__device__ __forceinline__ void agpr_acc_fence(f32x16& acc) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
+}
+
 // Workgroup index -> (sequence*head index bh, tile index t) for a grid of BH x NT
 // workgroups. Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on
 // XCD i % 8) and each XCD has its own L2.

@@ -43,8 +43,11 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-constexpr int kFwdWaves = 4;
-constexpr int kFwdThreads = 64 * kFwdWaves;
+// Four waves per workgroup. With two 32-query blocks per wave (one wave per SIMD, 512
+// registers) every K and V operand read from LDS feeds two MFMAs; with one block, two
+// workgroups share a compute unit (256 registers per wave).
+template <int QB> constexpr int fwd_waves() { return 4; }
+template <int QB> constexpr int fwd_occupancy() { return QB == 1 ? 2 : 1; }
 constexpr int kFwdBC = 64;        // keys per tile
 constexpr float kRescaleTau = 8.f;  // log2 growth of the row max tolerated before rescaling
 
@@ -66,86 +69,212 @@ struct FwdState {
   float l_run[QB];  // this lane's share of sum_j exp2(c * (s_j - m_run))
 };
 
-// One key tile for one wave: S^T, softmax update, O^T += V^T P^T.
-template <int D, int QB, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
-                                         int wq0, int lane, float c, bool mask) {
-  constexpr int NS = D / 16, NJ = kFwdBC / 32, NTK = kFwdBC / 16, NB = D / 32;
-  constexpr int KP = FwdLds<D>::KP, VP = FwdLds<D>::VP;
-  const int lr = lane & 31, g = lane >> 5;
+// The tile loop is software-pipelined by hand. A 64-key tile is two 32-key blocks, and
+// under the lazy rescale each block's softmax update stands on its own, so the
+// exponentials of one block run while the matrix pipe works on the other:
+//   S_0 | S_1 with exp(S_0) | P_0 V_0 with exp(S_1) | P_1 V_1
+// In each phase, operand reads run kPf steps ahead of the MFMA that uses them, and a
+// scheduling barrier closes every step, so the compiler neither sinks a read next to
+// its use (exposing the LDS latency) nor hoists all of them (a register per read).
+__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-  f32x16 sacc[QB][NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-    for (int n = 0; n < QB; ++n) sacc[n][j] = f32x16{};
-    const u16* arow = Ks + (32 * j + lr) * KP + 8 * g;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 a = ld16(arow + 16 * s);
-#pragma unroll
-      for (int n = 0; n < QB; ++n) sacc[n][j] = mfma32(a, st.qf[n][s], sacc[n][j]);
-    }
+constexpr int kFwdPf = 3;
+
+// O^T += V^T P^T step. With two query blocks per wave the O accumulators live in AGPRs
+// (see mfma32_agpr); with one they stay in VGPRs like everything else.
+template <int QB>
+__device__ __forceinline__ void fwd_pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (QB == 2) {
+    mfma32_agpr(acc, a, b);
+  } else {
+    acc = mfma32(a, b, acc);
   }
+}
 
-  bf16x8 pb[QB][NTK];
+template <int QB>
+__device__ __forceinline__ void fwd_o_fence(f32x16& acc) {
+  if constexpr (QB == 2) agpr_acc_fence(acc);
+}
+
+// K operand of S step s for key block j: row 32j + lane % 32 of the tile, head-dim
+// entries 16s + 8(lane / 32) + 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 fwd_k_operand(const u16* Ks, int j, int s, int lane) {
+  return ld16(Ks + (32 * j + (lane & 31)) * FwdLds<D>::KP + 8 * (lane >> 5) + 16 * s);
+}
+
+// V^T operand of PV step (bb, t): head-dim block bb, key slice 16t..16t+15 of the tile;
+// its k-slots are keys 16t + 4g + {0..3, 8..11}, matching the registers of P.
+template <int D>
+__device__ __forceinline__ bf16x8 fwd_v_operand(const u16* Vs, int bb, int t, int lane) {
+  return lds_tr_operand(Vs, FwdLds<D>::VP, 16 * t, 32 * bb, lane);
+}
+
+// Block j's scores: mask, row maxima (into m_new) and whether O and l need a rescale:
+// some row's maximum grew by more than 2^tau (always so on the first visible block,
+// where m_run is -inf). The decision is taken for the whole wave.
+template <int D, int QB, bool CAUSAL>
+__device__ __forceinline__ bool fwd_block_stats(const FwdState<D, QB>& st, f32x16 (&sj)[QB], float (&m_new)[QB],
+                                                int kb0, int len, int wq0, int lane, float c, bool mask) {
+  const int lr = lane & 31, g = lane >> 5;
+  bool grow = false;
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
     if (mask) {  // wave-uniform: a diagonal or tail tile
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * j + crow_nat(r, g);
-          const bool hide = key >= len || (CAUSAL && key > qi);
-          sacc[n][j][r] = hide ? -INFINITY : sacc[n][j][r];
-        }
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[n][j][r]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(st.m_run[n], mx);
-    // Rescale when this row's maximum grew by more than 2^tau (always on the first
-    // visible tile, where m_run is -inf); the decision is taken for the whole wave.
-    const bool grow = (m_new - st.m_run[n]) * c > kRescaleTau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_to = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2((st.m_run[n] - m_to) * c);
-      st.m_run[n] = m_new;
-      st.l_run[n] *= alpha;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) st.oacc[n][bb] *= alpha;
-    }
-    const float nb = st.m_run[n] == -INFINITY ? 0.f : -st.m_run[n] * c;
-    float ls = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(sacc[n][j][r], c, nb));
-        sacc[n][j][r] = e;
-        ls += e;
+        const int key = kb0 + crow_nat(r, g);
+        const bool hide = key >= len || (CAUSAL && key > qi);
+        sj[n][r] = hide ? -INFINITY : sj[n][r];
       }
     }
-    st.l_run[n] += ls;
+    float mx = sj[n][0];
 #pragma unroll
-    for (int t = 0; t < NTK; ++t) pb[n][t] = to_bf16x8(half_of(sacc[n][t >> 1], t & 1));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sj[n][r]);
+    m_new[n] = fmaxf(st.m_run[n], pair_max(mx));
+    grow |= (m_new[n] - st.m_run[n]) * c > kRescaleTau;
+  }
+  return __builtin_amdgcn_ballot_w64(grow) != 0;
+}
+
+// Move the reference maximum to m_new and scale l to match; returns the factor that O
+// must be scaled by (the caller does it once every product formed under the old
+// reference has been added).
+template <int D, int QB>
+__device__ __forceinline__ void fwd_move_ref(FwdState<D, QB>& st, const float (&m_new)[QB], float c,
+                                             float (&alpha)[QB]) {
+#pragma unroll
+  for (int n = 0; n < QB; ++n) {
+    const float m_to = m_new[n] == -INFINITY ? 0.f : m_new[n];
+    alpha[n] = fast_exp2((st.m_run[n] - m_to) * c);
+    st.m_run[n] = m_new[n];
+    st.l_run[n] *= alpha[n];
+  }
+}
+
+template <int D, int QB>
+__device__ __forceinline__ void fwd_scale_o(FwdState<D, QB>& st, const float (&alpha)[QB]) {
+#pragma unroll
+  for (int n = 0; n < QB; ++n)
+#pragma unroll
+    for (int bb = 0; bb < D / 32; ++bb) {
+      fwd_o_fence<QB>(st.oacc[n][bb]);
+      st.oacc[n][bb] *= alpha[n];
+    }
+}
+
+// One exponential of block j's scores (value v of QB * 16), its share of the row sum,
+// and, every eighth value, the bf16 conversion of eight of them into P.
+template <int QB>
+__device__ __forceinline__ void fwd_exp_one(f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4],
+                                            const float (&nb)[QB], float c, int v) {
+  const int n = v / 16, r = v % 16;
+  float e = fast_exp2(fmaf(sj[n][r], c, nb[n]));
+  // Pin the exponential to this step: without it the compiler sinks the whole softmax
+  // towards its first use, out of the matrix-pipe phase it is meant to overlap.
+  asm volatile("" : "+v"(e));
+  sj[n][r] = e;
+  ls[n][r & 3] += e;
+  if (r % 8 == 7) pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
+}
+
+template <int QB>
+__device__ __forceinline__ void fwd_exp_begin(const float (&m_run)[QB], float c, float (&nb)[QB],
+                                              float (&ls)[QB][4]) {
+#pragma unroll
+  for (int n = 0; n < QB; ++n) {
+    nb[n] = m_run[n] == -INFINITY ? 0.f : -m_run[n] * c;
+    ls[n][0] = ls[n][1] = ls[n][2] = ls[n][3] = 0.f;
+  }
+}
+
+// One key tile for one wave: S^T = K Q^T, softmax update, O^T += V^T P^T.
+template <int D, int QB, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
+                                         int wq0, int lane, float c, bool mask) {
+  constexpr int NS = D / 16, NB = D / 32, E = 16 * QB;
+  constexpr int TP = 2 * NB;  // PV steps per key block: (bb, t) for t in the block's two slices
+  static_assert(E % NS == 0 && E % TP == 0, "exponentials must split evenly over the steps");
+
+  f32x16 s0[QB], s1[QB];
+#pragma unroll
+  for (int n = 0; n < QB; ++n) s0[n] = s1[n] = f32x16{};
+
+  // S_0
+  {
+    bf16x8 a[NS];
+#pragma unroll
+    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 0, s, lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 0, s + kFwdPf, lane);
+#pragma unroll
+      for (int n = 0; n < QB; ++n) s0[n] = mfma32(a[s], st.qf[n][s], s0[n]);
+      step_fence();
+    }
+  }
+  float m_new[QB], alpha[QB];
+  if (fwd_block_stats<D, QB, CAUSAL>(st, s0, m_new, k0, len, wq0, lane, c, mask)) {
+    fwd_move_ref<D, QB>(st, m_new, c, alpha);
+    fwd_scale_o<D, QB>(st, alpha);
   }
 
-  // O^T += V^T P^T: A row m of block bb is head-dim entry 32bb + m; the k-slots of lane
-  // group g at step t are keys 16t + 4g + {0..3, 8..11}, matching the P registers.
+  // S_1 with exp(S_0)
+  bf16x8 p0[QB][2], p1[QB][2];
+  float nb[QB], ls[QB][4];
+  fwd_exp_begin<QB>(st.m_run, c, nb, ls);
+  {
+    bf16x8 a[NS];
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
+    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 1, s, lane);
 #pragma unroll
-    for (int t = 0; t < NTK; ++t) {
-      const bf16x8 a = lds_tr_operand(Vs, VP, 16 * t, 32 * bb, lane);
+    for (int s = 0; s < NS; ++s) {
+      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 1, s + kFwdPf, lane);
 #pragma unroll
-      for (int n = 0; n < QB; ++n) st.oacc[n][bb] = mfma32(a, pb[n][t], st.oacc[n][bb]);
+      for (int n = 0; n < QB; ++n) s1[n] = mfma32(a[s], st.qf[n][s], s1[n]);
+#pragma unroll
+      for (int u = 0; u < E / NS; ++u) fwd_exp_one<QB>(s0, p0, ls, nb, c, s * (E / NS) + u);
+      step_fence();
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
+  const bool grow1 = fwd_block_stats<D, QB, CAUSAL>(st, s1, m_new, k0 + 32, len, wq0, lane, c, mask);
+  if (grow1) fwd_move_ref<D, QB>(st, m_new, c, alpha);
+
+  // P_0 V_0 with exp(S_1). If block 1 moved the reference maximum, P_0 (formed under
+  // the old one) still joins O first and O is scaled right after.
+  fwd_exp_begin<QB>(st.m_run, c, nb, ls);
+  {
+    bf16x8 a[TP];
+#pragma unroll
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, i & 1, lane);
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, (i + kFwdPf) & 1, lane);
+#pragma unroll
+      for (int n = 0; n < QB; ++n) fwd_pv_mfma<QB>(st.oacc[n][i >> 1], a[i], p0[n][i & 1]);
+#pragma unroll
+      for (int u = 0; u < E / TP; ++u) fwd_exp_one<QB>(s1, p1, ls, nb, c, i * (E / TP) + u);
+      step_fence();
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
+  if (grow1) fwd_scale_o<D, QB>(st, alpha);
+
+  // P_1 V_1
+  {
+    bf16x8 a[TP];
+#pragma unroll
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, 2 + (i & 1), lane);
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, 2 + ((i + kFwdPf) & 1), lane);
+#pragma unroll
+      for (int n = 0; n < QB; ++n) fwd_pv_mfma<QB>(st.oacc[n][i >> 1], a[i], p1[n][i & 1]);
+      step_fence();
     }
   }
 }
@@ -153,8 +282,9 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
 // Two query blocks per wave need the whole register file (one workgroup per compute
 // unit); so does the non-causal head_dim 128 variant, which spills at two.
 template <int D, bool CAUSAL, bool VARLEN, int QB>
-__global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 : 1) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int BR = 32 * QB * kFwdWaves, BC = kFwdBC, NT = kFwdThreads;
+__global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int NW = fwd_waves<QB>();
+  constexpr int BR = 32 * QB * NW, BC = kFwdBC;
   constexpr int NB = D / 32, NS = D / 16;
   using L = FwdLds<D>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
@@ -205,8 +335,8 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  TileDma<BC, D, L::KP, kFwdWaves> kdma;
-  TileDma<BC, D, L::VP, kFwdWaves> vdma;
+  TileDma<BC, D, L::KP, NW> kdma;
+  TileDma<BC, D, L::VP, NW> vdma;
   kdma.init(stride, w, lane);
   vdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
@@ -237,6 +367,10 @@ __global__ __launch_bounds__(kFwdThreads, (QB == 1 && (CAUSAL || D == 64)) ? 2 :
     __syncthreads();
   }
 
+#pragma unroll
+  for (int n = 0; n < QB; ++n)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) fwd_o_fence<QB>(st.oacc[n][bb]);
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
@@ -269,7 +403,7 @@ hipError_t launch_fwd_t(const Problem& pr) {
   // Two query blocks per wave halve the LDS reads per MFMA; at head_dim 128 their
   // accumulators no longer fit the register file, so one block is used there.
   constexpr int QB = D == 64 ? 2 : 1;
-  constexpr int BR = 32 * QB * kFwdWaves;
+  constexpr int BR = 32 * QB * fwd_waves<QB>();
   FwdParams p;
   p.q = static_cast<const u16*>(pr.q);
   p.k = static_cast<const u16*>(pr.k);
@@ -285,7 +419,7 @@ hipError_t launch_fwd_t(const Problem& pr) {
   p.scale = pr.scale;
   p.c = pr.scale * kLog2e;
   const dim3 grid((unsigned)(p.n_qtiles * pr.batch * pr.heads));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, QB>), grid, dim3(kFwdThreads), 0, pr.stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, QB>), grid, dim3(64 * fwd_waves<QB>()), 0, pr.stream, p);
   return hipGetLastError();
 }
 
