@@ -34,11 +34,12 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file additions. The forward kernel runs one wave per SIMD with its output
-# accumulators pinned in AGPRs by inline asm; every other MFMA there must use the VGPR
+# Per-file additions. Where a kernel pins its output accumulators in AGPRs by inline asm
+# (forward at head_dim 64, dK/dV at head_dim 128), every other MFMA must use the VGPR
 # form, so the score accumulators stay where the softmax arithmetic reads them.
 FILE_FLAGS = {
     "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

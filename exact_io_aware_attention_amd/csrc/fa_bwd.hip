@@ -135,6 +135,22 @@ struct KvState {
 //   P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D);
 //   dV^T += dO^T P and dK^T += Q^T dS, whose A rows (head-dim entries) are read
 //   transposed from the row-major tiles with k-slots queries 16t + 4g + {0..3, 8..11}.
+// dV^T / dK^T accumulation step. At head_dim 128 the accumulators (128 registers) are
+// pinned in AGPRs, leaving the VGPRs to the score arithmetic; at 64 they fit anyway.
+template <int D>
+__device__ __forceinline__ void kv_acc_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (D == 128) {
+    mfma32_agpr(acc, a, b);
+  } else {
+    acc = mfma32(a, b, acc);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_acc_fence(f32x16& acc) {
+  if constexpr (D == 128) agpr_acc_fence(acc);
+}
+
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int len, bool mask,
                                           int lane, float c) {
@@ -196,11 +212,11 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
       aqt[i] = lds_tr_operand(Qs, P, 32 * a + 16 * (i & 1), 32 * (i >> 1), lane);
-      st.dvT[i >> 1] = mfma32(aot[i], (i & 1) ? pb1 : pb0, st.dvT[i >> 1]);
+      kv_acc_mfma<D>(st.dvT[i >> 1], aot[i], (i & 1) ? pb1 : pb0);
     }
     const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
 #pragma unroll
-    for (int i = 0; i < 2 * NB; ++i) st.dkT[i >> 1] = mfma32(aqt[i], (i & 1) ? ds1 : ds0, st.dkT[i >> 1]);
+    for (int i = 0; i < 2 * NB; ++i) kv_acc_mfma<D>(st.dkT[i >> 1], aqt[i], (i & 1) ? ds1 : ds0);
   }
 }
 
@@ -304,6 +320,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     __syncthreads();
   }
 
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    kv_acc_fence<D>(st.dvT[bb]);
+    kv_acc_fence<D>(st.dkT[bb]);
+  }
   if (kj >= len) return;
   u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
   u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
