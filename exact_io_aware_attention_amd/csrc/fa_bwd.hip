@@ -353,8 +353,10 @@ constexpr int kDqBC = 64;             // keys per tile
 // (row-wise for dP^T).
 template <int D>
 struct DqLds {
+  // V is read row-wise only, but pitch_both is conflict-free for row reads too, and one
+  // pitch for both tiles lets a single set of copy offsets serve K and V.
   static constexpr int KP = pitch_both<D>();
-  static constexpr int VP = pitch_rows<D>();
+  static constexpr int VP = pitch_both<D>();
   static constexpr int KSZ = kDqBC * KP;
   static constexpr int BUF = KSZ + kDqBC * VP;
 };
@@ -480,13 +482,12 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
-  TileDma<BC, D, L::KP, kDqWaves> kdma;
-  TileDma<BC, D, L::VP, kDqWaves> vdma;
-  kdma.init(stride, w, lane);
-  vdma.init(stride, w, lane);
+  static_assert(L::KP == L::VP, "K and V tiles share their copy offsets");
+  TileDma<BC, D, L::KP, kDqWaves> kvdma;
+  kvdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
-    kdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
-    vdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
+    kvdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
+    kvdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
   };
   auto compute = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;
