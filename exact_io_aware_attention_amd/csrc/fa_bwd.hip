@@ -109,16 +109,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
-constexpr int kKvBQ = 64;             // queries per tile
+// Queries per tile: 128 halves the barriers and copies per query; under causal masking
+// 64, since the first tile of each key range is partly above the diagonal and a larger
+// tile wastes more there (a per-block skip would break the interleaving of blocks).
+template <bool CAUSAL> constexpr int kv_bq() { return CAUSAL ? 64 : 128; }
 
 // One double-buffered half: Q and dO tiles (row-major; read both row-wise for S and
 // dP and through transpose reads for dK and dV), then LSE*log2(e) and D per query.
-template <int D>
+template <int D, int BQ>
 struct KvLds {
   static constexpr int P = pitch_both<D>();
-  static constexpr int TSZ = kKvBQ * P;            // elements of one tile
+  static constexpr int TSZ = BQ * P;               // elements of one tile
   static constexpr int STAT = 2 * TSZ;             // u16 offset of the fp32 statistics
-  static constexpr int BUF = 2 * TSZ + 4 * kKvBQ;  // + lse and D (2 x BQ floats)
+  static constexpr int BUF = 2 * TSZ + 4 * BQ;     // + lse and D (2 x BQ floats)
 };
 
 template <int D>
@@ -154,12 +157,14 @@ __device__ __forceinline__ void kv_acc_fence(f32x16& acc) {
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int len, bool mask,
                                           int lane, float c) {
-  constexpr int NB = D / 32, NS = D / 16, NA = kKvBQ / 32;
-  constexpr int P = KvLds<D>::P;
+  constexpr int BQ = kv_bq<CAUSAL>();
+  using L = KvLds<D, BQ>;
+  constexpr int NB = D / 32, NS = D / 16, NA = BQ / 32;
+  constexpr int P = L::P;
   const u16* Qs = buf;
-  const u16* dOs = buf + KvLds<D>::TSZ;
-  const float* lse_s = reinterpret_cast<const float*>(buf + KvLds<D>::STAT);
-  const float* dd_s = lse_s + kKvBQ;
+  const u16* dOs = buf + L::TSZ;
+  const float* lse_s = reinterpret_cast<const float*>(buf + L::STAT);
+  const float* dd_s = lse_s + BQ;
   const int lr = lane & 31, g = lane >> 5;
 
 #pragma unroll
@@ -222,9 +227,9 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
-  constexpr int BK = kKvBK, BQ = kKvBQ, NT = kKvThreads;
+  constexpr int BK = kKvBK, BQ = kv_bq<CAUSAL>(), NT = kKvThreads;
   constexpr int NB = D / 32, NS = D / 16;
-  using L = KvLds<D>;
+  using L = KvLds<D, BQ>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
 
