@@ -115,6 +115,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (not varlen)")
+    ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (not varlen)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the warmup, run a plain fp32 copy kernel (y = -x) over this many MiB, "
                          "three times, as the known-size reference for HBM byte counters")
@@ -134,7 +136,11 @@ def main(argv=None) -> int:
         return 1
     w = W.get(a.workload)
     log(f"bench: generating {w.name} inputs")
-    inp = W.make_inputs(w)
+    if (a.batch is not None or a.seqlen is not None) and w.varlen:
+        print("--batch/--seqlen apply to fixed-length workloads only", file=sys.stderr)
+        return 2
+    inp = W.make_inputs(w, batch=a.batch, seqlen=a.seqlen)
+    resized = a.batch is not None or a.seqlen is not None
     dev = torch.device("cuda:0")
     q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
     cu = inp.cu_seqlens.to(dev) if inp.cu_seqlens is not None else None
@@ -212,7 +218,7 @@ def main(argv=None) -> int:
     value = (fwd_fl + bwd_fl) / (step_ms * 1e-3) / 1e12
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
     achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
-    tr = traffic_for(w.name, dom)
+    tr = None if resized else traffic_for(w.name, dom)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -228,7 +234,7 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded iid normal inputs)",
         "config": {
-            "workload": f"{w.name}: {w.description}",
+            "workload": f"{w.name}: {w.description}" + (" (resized)" if resized else ""),
             "batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": bool(w.causal),
             "global_batch": B, "parallelism": "single GPU",
         },
