@@ -37,7 +37,7 @@ struct BwdParams {
   u16* dv;
   const int32_t* cu;
   int B, H, N, T;
-  int n_tiles;  // query tiles (dq) or key tiles (dkdv) per sequence
+  int n_tiles;  // workgroups per (sequence, head): key tiles (dkdv) or query-tile slots (dq)
   float scale;
   float c;      // scale * log2(e)
 };
@@ -435,33 +435,19 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
   }
 }
 
-// Two workgroups per compute unit (two waves per SIMD) keep the matrix pipe busy while
-// the other wave waits on LDS or does its softmax arithmetic.
+// One query tile of one (sequence, head) of the dQ pass. The two LDS buffers are free
+// again when it returns (its last step ends in a barrier).
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
-  constexpr int BR = kDqBR, BC = kDqBC, NT = kDqThreads;
+__device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
+                                         u16* buf1) {
+#if __HIP_DEVICE_COMPILE__
+  constexpr int BR = kDqBR, BC = kDqBC;
   constexpr int NB = D / 32, NS = D / 16;
   using L = DqLds<D>;
-  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
-  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
-
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-
-  int bh, qt;
-  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, CAUSAL, false, bh, qt);
-  const int b = bh / p.H, h = bh % p.H;
-  int start, len;
-  if (VARLEN) {
-    start = p.cu[b];
-    len = p.cu[b + 1] - start;
-  } else {
-    start = b * p.N;
-    len = p.N;
-  }
   const int q0 = qt * BR;
-  if (q0 >= len) return;
 
   const size_t stride = (size_t)p.H * D;
   const size_t base = ((size_t)start * p.H + h) * D;
@@ -527,6 +513,40 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
                    st.dqT[bb][4 * a + 2] * p.scale, st.dqT[bb][4 * a + 3] * p.scale);
     }
   }
+#endif
+}
+
+// Two workgroups per compute unit (two waves per SIMD) keep the matrix pipe busy while
+// the other wave waits on LDS or does its softmax arithmetic. Workgroup -> (sequence,
+// head, slot) as in the forward: head-grouped per XCD; under causal masking slot i takes
+// query tiles nt-1-i and i, so every workgroup visits the same number of key tiles.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
+  using L = DqLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
+
+  int bh, slot;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, false, true, bh, slot);
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int nt = (len + kDqBR - 1) / kDqBR;
+  if (CAUSAL) {
+    const int t_hi = nt - 1 - slot;
+    if (t_hi < slot) return;
+    dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, t_hi, buf0, buf1);
+    if (slot < t_hi) dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);
+  } else {
+    if (slot >= nt) return;
+    dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);
+  }
 }
 
 // ------------------------------------------------------------------------ launch
@@ -583,7 +603,8 @@ hipError_t launch_dkdv_t(const Problem& pr) {
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dq_t(const Problem& pr) {
   BwdParams p = make_params(pr);
-  p.n_tiles = (pr.seqlen + kDqBR - 1) / kDqBR;
+  const int n_qtiles = (pr.seqlen + kDqBR - 1) / kDqBR;
+  p.n_tiles = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // workgroup slots per (sequence, head)
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, VARLEN>),
                      dim3((unsigned)(p.n_tiles * pr.batch * pr.heads)), dim3(kDqThreads), 0, pr.stream, p);
   return hipGetLastError();

@@ -38,7 +38,7 @@ struct FwdParams {
   float* lse;
   const int32_t* cu;
   int B, H, N, T;
-  int n_qtiles;
+  int n_slots;  // workgroups per (sequence, head)
   float scale;
   float c;  // scale * log2(e)
 };
@@ -279,36 +279,20 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
   }
 }
 
-// Two query blocks per wave need the whole register file (one workgroup per compute
-// unit); so does the non-causal head_dim 128 variant, which spills at two.
+// One query tile of one (sequence, head): the key loop and the epilogue. The two LDS
+// buffers are free again when it returns (its last step ends in a barrier).
 template <int D, bool CAUSAL, bool VARLEN, int QB>
-__global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd_bf16_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
+                                          u16* buf1) {
+#if __HIP_DEVICE_COMPILE__
   constexpr int NW = fwd_waves<QB>();
   constexpr int BR = 32 * QB * NW, BC = kFwdBC;
   constexpr int NB = D / 32, NS = D / 16;
   using L = FwdLds<D>;
-  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
-  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
-
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-
-  // Workgroup -> (sequence, head, query tile), tile-major; causal tiles near the end of
-  // a sequence have the most keys to visit, so they are issued first.
-  int bh, qt;
-  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_qtiles, CAUSAL, false, bh, qt);
-  const int b = bh / p.H, h = bh % p.H;
-  int start, len;
-  if (VARLEN) {
-    start = p.cu[b];
-    len = p.cu[b + 1] - start;
-  } else {
-    start = b * p.N;
-    len = p.N;
-  }
   const int q0 = qt * BR;
-  if (q0 >= len) return;
 
   const size_t stride = (size_t)p.H * D;
   const size_t base = ((size_t)start * p.H + h) * D;
@@ -396,6 +380,43 @@ __global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd
       p.lse[li] = st.m_run[n] * p.scale + logf(l_tot);
     }
   }
+#endif
+}
+
+// Two query blocks per wave need the whole register file (one workgroup per compute
+// unit). Workgroup -> (sequence, head, slot): head-grouped per XCD, so the workgroups
+// resident on one XCD share few heads and stream the same K/V rows through its L2 (this
+// keeps the fabric traffic near the O(N d) operand bytes at long sequences). Without
+// masking a slot is one query tile; under causal masking tile t visits t + 1 key tiles,
+// so slot i takes tiles nt-1-i and i and every workgroup does the same work.
+template <int D, bool CAUSAL, bool VARLEN, int QB>
+__global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int BR = 32 * QB * fwd_waves<QB>();
+  using L = FwdLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
+
+  int bh, slot;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_slots, false, true, bh, slot);
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int nt = (len + BR - 1) / BR;
+  if (CAUSAL) {
+    const int t_hi = nt - 1 - slot;
+    if (t_hi < slot) return;
+    fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, t_hi, buf0, buf1);
+    if (slot < t_hi) fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, slot, buf0, buf1);
+  } else {
+    if (slot >= nt) return;
+    fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, slot, buf0, buf1);
+  }
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -415,10 +436,11 @@ hipError_t launch_fwd_t(const Problem& pr) {
   p.H = pr.heads;
   p.N = pr.seqlen;
   p.T = pr.total_tokens;
-  p.n_qtiles = (pr.seqlen + BR - 1) / BR;
+  const int n_qtiles = (pr.seqlen + BR - 1) / BR;
+  p.n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
   p.scale = pr.scale;
   p.c = pr.scale * kLog2e;
-  const dim3 grid((unsigned)(p.n_qtiles * pr.batch * pr.heads));
+  const dim3 grid((unsigned)(p.n_slots * pr.batch * pr.heads));
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, QB>), grid, dim3(64 * fwd_waves<QB>()), 0, pr.stream, p);
   return hipGetLastError();
 }
