@@ -41,7 +41,24 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # the ratio that the same counter shows for a copy kernel of known size run in the same
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
-TRAFFIC = {}
+TRAFFIC = {
+    ("c3", "fwd"): {"bytes": 753262813, "fetch_kib": 301250.3, "write_kib": 133122.5,
+                  "fetch_factor": 2.0, "write_factor": 1.0,
+                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "profile": "profiles/attention_fwd_bwd_c3.md"},
+    ("c3", "bwd_preprocess"): {"bytes": 276875849, "fetch_kib": 131100.5, "write_kib": 8192.0,
+                  "fetch_factor": 2.0, "write_factor": 1.0,
+                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "profile": "profiles/attention_fwd_bwd_c3.md"},
+    ("c3", "bwd_dkdv"): {"bytes": 964630313, "fetch_kib": 337108.7, "write_kib": 267821.0,
+                  "fetch_factor": 2.0, "write_factor": 1.0,
+                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "profile": "profiles/attention_fwd_bwd_c3.md"},
+    ("c3", "bwd_dq"): {"bytes": 914367416, "fetch_kib": 378807.0, "write_kib": 135341.7,
+                  "fetch_factor": 2.0, "write_factor": 1.0,
+                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "profile": "profiles/attention_fwd_bwd_c3.md"},
+}
 
 
 def sources_sha256() -> str:
