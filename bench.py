@@ -89,6 +89,60 @@ def gemm_unit(B, H, N, d, causal, lengths=None):
     return 2.0 * B * H * N * N * d * (0.5 if causal else 1.0)
 
 
+def standard_attention(q, k, v, do, scale: float, causal: bool, reps: int = 3):
+    """Standard (materialising) attention on the same GPU, for comparison: S = scale Q K^T
+    and P = softmax(S) are written to HBM as full N x N matrices (bf16 GEMMs with fp32
+    accumulation via torch.matmul, softmax in fp32), and the backward is the textbook
+    chain rule on those stored matrices. Every matmul gets contiguous operands. Returns
+    fwd/bwd times (median of `reps`, HIP events on the current stream), the peak device
+    memory the two passes allocate, and O for a sanity check."""
+    import torch
+    B, N, H, d = q.shape
+    qh, kh, vh, doh = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v, do))  # (B, H, N, d)
+    kt = kh.transpose(-1, -2).contiguous()
+    vt = vh.transpose(-1, -2).contiguous()
+    mask = torch.ones(N, N, device=q.device, dtype=torch.bool).triu_(1) if causal else None
+
+    def fwd():
+        s = torch.matmul(qh, kt).float().mul_(scale)
+        if mask is not None:
+            s.masked_fill_(mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).to(q.dtype)
+        del s
+        return p, torch.matmul(p, vh)
+
+    def bwd(p, o):
+        dv = torch.matmul(p.transpose(-1, -2).contiguous(), doh)
+        dp = torch.matmul(doh, vt).float()
+        dd = (doh.float() * o.float()).sum(-1, keepdim=True)
+        ds = (p.float() * (dp - dd)).to(q.dtype)
+        del dp
+        dq = torch.matmul(ds, kh).float().mul_(scale)
+        dk = torch.matmul(ds.transpose(-1, -2).contiguous(), qh).float().mul_(scale)
+        return dq, dk, dv
+
+    stream = torch.cuda.current_stream()
+    tf, tb = [], []
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o = None
+    for _ in range(reps + 1):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        p, o = fwd()
+        e1.record(stream)
+        grads = bwd(p, o)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        tf.append(e0.elapsed_time(e1))
+        tb.append(e1.elapsed_time(e2))
+        del p, grads
+    peak = torch.cuda.max_memory_allocated() - base
+    med = lambda x: sorted(x[1:])[len(x[1:]) // 2]
+    return {"fwd_ms": med(tf), "bwd_ms": med(tb), "peak_extra_bytes": int(peak)}, o.permute(0, 2, 1, 3)
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """Time the oracle (fp64, NumPy) on whole heads of the workload until ~budget_s."""
     import numpy as np
@@ -134,6 +188,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (not varlen)")
     ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (not varlen)")
+    ap.add_argument("--no-standard", action="store_true",
+                    help="skip the standard-attention comparison (materialised N x N scores)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the warmup, run a plain fp32 copy kernel (y = -x) over this many MiB, "
                          "three times, as the known-size reference for HBM byte counters")
@@ -277,6 +333,25 @@ def main(argv=None) -> int:
             "fetch_factor": tr["fetch_factor"], "write_factor": tr["write_factor"],
             "achieved_hbm_gbs": round(tr["bytes"] / (per[dom] * 1e-3) / 1e9, 1),
             "profile": tr["profile"]}
+    need = 3 * B * H * N * N * 4  # fp32 scores + bf16 copies, roughly
+    total_mem = torch.cuda.get_device_properties(0).total_memory
+    if not a.no_standard and w.varlen is False and w.dtype == "bf16" and need > total_mem // 2:
+        out["standard_attention"] = {"skipped": f"needs about {need / 2**30:.0f} GiB for the N x N matrices "
+                                                f"(device: {total_mem / 2**30:.0f} GiB)"}
+    elif not a.no_standard and w.varlen is False and w.dtype == "bf16":
+        # The same step with standard attention; its memory is what this library avoids.
+        log("bench: standard attention (materialised scores) for comparison")
+        st, o_std = standard_attention(q, k, v, do, w.scale, bool(w.causal))
+        ours_fwd, ours_bwd = per["fwd"], bwd_ms
+        out["standard_attention"] = {
+            "fwd_ms": round(st["fwd_ms"], 4), "bwd_ms": round(st["bwd_ms"], 4),
+            "speedup_fwd": round(st["fwd_ms"] / ours_fwd, 2), "speedup_bwd": round(st["bwd_ms"] / ours_bwd, 2),
+            "peak_extra_gib": round(st["peak_extra_bytes"] / 2**30, 2),
+            "ours_workspace_gib": round(ws_bytes / 2**30, 4),
+            "o_max_abs_diff": round(float((o_std.float() - o.float()).abs().max()), 4),
+        }
+        del o_std
+        torch.cuda.empty_cache()
     if a.cpu_budget > 0 and w.varlen is False:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)
