@@ -17,4 +17,6 @@ from .attention import (  # noqa: F401
     forward_rows,
     backward_query_rows,
     backward_key_rows,
+    head_decode,
+    decode,
 )

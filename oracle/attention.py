@@ -50,6 +50,10 @@ supports):
       logsumexp of the scaled, masked scores.
 * r5  packed batches ([MS] "Con Sequence Packing"): attention is block-diagonal per
       sequence; causal applies within each sequence.
+* r15 decoding (the pages cite faster inference without a formula): Nq new queries
+      attend to a cache of Nk keys of which they are the last Nq positions; under
+      causal masking query i (0-based) sees key j iff j <= Nk - Nq + i (bottom-right
+      alignment; with Nq = Nk this is r2).
 
 Every function here is pinned by tests that do not retype it: closed forms, hand
 derived worked values (tests/golden), invariants, central finite differences,
@@ -127,6 +131,30 @@ def head_backward(q: Array, k: Array, v: Array, do: Array, scale: float,
 # ----------------------------------------------------------------------------------------
 # Whole tensors: (B, N, H, d) padded batches, or (T, H, d) packed with cu_seqlens.
 # ----------------------------------------------------------------------------------------
+
+def head_decode(q: Array, k: Array, v: Array, scale: float, causal: bool) -> Tuple[Array, Array]:
+    """Nq queries against Nk cached keys (reading r15): O (Nq, d) and LSE (Nq,)."""
+    n_q, n_k = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        last_visible = n_k - n_q + np.arange(n_q)  # the absolute position of each query
+        s = np.where(np.arange(n_k)[None, :] > last_visible[:, None], -np.inf, s)
+    p, lse = _softmax_rows(s)
+    return p @ v, lse
+
+
+def decode(q, k, v, scale: float, causal: bool) -> Tuple[Array, Array]:
+    """Batched decode: q (B, Nq, H, d), k and v (B, Nk, H, d); O (B, Nq, H, d) and LSE
+    (B, H, Nq)."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, n_q, H, _ = q.shape
+    o = np.zeros((B, n_q, H, v.shape[-1]))
+    lse = np.zeros((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            o[b, :, h, :], lse[b, h, :] = head_decode(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal)
+    return o, lse
+
 
 def _segments(shape, cu_seqlens) -> Sequence[Tuple[Optional[int], int, int]]:
     """(batch index or None, token start, token end) of each sequence."""

@@ -41,6 +41,10 @@ MUTATIONS = {
     "key_rows_d_from_do": ("d_row = (do[rows] * o_rows)", "d_row = (do[rows] * do[rows])"),
     "key_rows_dk_unscaled": ("dk += scale * (ds_sel.T @ q[rows])", "dk += (ds_sel.T @ q[rows])"),
     "packed_lse_layout": ("lse[h, t0:t1] = lh", "lse[h, t0:t1] = lh[::-1]"),
+    "decode_top_left_alignment": ("last_visible = n_k - n_q + np.arange(n_q)", "last_visible = np.arange(n_q)"),
+    "decode_mask_off_by_one": ("np.arange(n_k)[None, :] > last_visible[:, None]",
+                               "np.arange(n_k)[None, :] >= last_visible[:, None]"),
+    "decode_lse_layout": ("o[b, :, h, :], lse[b, h, :] = head_decode", "lse[b, h, :], o[b, :, h, :] = head_decode"),
 }
 
 
@@ -151,8 +155,25 @@ def _pins(m):
             np.testing.assert_allclose(o[t, 0], want, atol=1e-12)
             np.testing.assert_allclose(lse[0, t], math.log(sum(w)), atol=1e-12)
 
+    def decode():
+        rng = np.random.default_rng(5)
+        B, n_q, n_k, H, d = 1, 3, 11, 2, 4
+        q, k, v = (rng.standard_normal((B, n, H, d)) for n in (n_q, n_k, n_k))
+        for causal in (False, True):
+            o, lse = m.decode(q, k, v, 0.6, causal)
+            for h in range(H):
+                tq, tk, tv = (torch.tensor(x[0, :, h])[None, None] for x in (q, k, v))
+                allowed = torch.arange(n_k)[None, :] <= (n_k - n_q + torch.arange(n_q))[:, None]
+                mask = allowed[None, None] if causal else None
+                to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.6)[0, 0]
+                np.testing.assert_allclose(o[0, :, h], to.numpy(), atol=1e-12)
+                s = 0.6 * tq[0, 0] @ tk[0, 0].T
+                if causal:
+                    s = s.masked_fill(~allowed, float("-inf"))
+                np.testing.assert_allclose(lse[0, h], torch.logsumexp(s, 1).numpy(), atol=1e-12)
+
     for name, fn in (("golden", golden), ("torch", torch_ref), ("fd", finite_differences),
-                     ("rows", row_helpers), ("packed", packed)):
+                     ("rows", row_helpers), ("packed", packed), ("decode", decode)):
         check(name, fn)
     return failed
 
