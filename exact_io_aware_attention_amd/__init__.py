@@ -65,6 +65,10 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_dq.restype = i32
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
+    lib.fa_fwd_decode.restype = i32
+    lib.fa_fwd_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_fwd_decode_workspace_bytes.restype = sz
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -116,6 +120,19 @@ def fa_bwd_dq(q: int, k: int, v: int, dout: int, lse: int, workspace: int, works
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen: int, head_dim: int, varlen: int,
                            total_tokens: int) -> int:
     return load_library().fa_bwd_workspace_bytes(batch, heads, seqlen, head_dim, int(varlen), total_tokens)
+
+
+def fa_fwd_decode(q: int, k: int, v: int, o: int, lse: int, batch: int, heads: int, seqlen_q: int,
+                  seqlen_k: int, head_dim: int, softmax_scale: float, causal: int, num_splits: int,
+                  workspace: int, workspace_bytes: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_fwd_decode(q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, head_dim,
+                                        softmax_scale, int(causal), num_splits, workspace, workspace_bytes,
+                                        dtype, stream)
+
+
+def fa_fwd_decode_workspace_bytes(batch: int, heads: int, seqlen_q: int, seqlen_k: int, head_dim: int,
+                                  num_splits: int) -> int:
+    return load_library().fa_fwd_decode_workspace_bytes(batch, heads, seqlen_q, seqlen_k, head_dim, num_splits)
 
 
 def fa_strerror(status: int) -> str:
@@ -199,3 +216,30 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def decode(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, num_splits: int = 0,
+           out=None, lse=None, workspace=None, stream=None) -> Tuple:
+    """O and LSE of seqlen_q (<= 32) new queries against a cache of seqlen_k keys/values
+    (see fa_fwd_decode in include/fa.h). q: (batch, seqlen_q, heads, head_dim); k, v:
+    (batch, seqlen_k, heads, head_dim); bf16."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be (batch, seqlen, heads, head_dim)")
+    _check(q, k, v)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    ws_bytes = fa_fwd_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
+    st = fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                       scale, int(causal), num_splits, workspace.data_ptr(), workspace.numel(), _dtype_code(q),
+                       _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_decode")
+    return out, lse

@@ -61,6 +61,38 @@ int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batc
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Checks of the decode entry points; fills the sizes and the split choice of `pr` and
+// the workspace it needs.
+int check_decode(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                 int num_splits, int dtype, fa::DecodeProblem& pr, size_t* need) {
+  if (batch < 1 || heads < 1 || seqlen_q < 1 || seqlen_k < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (causal && seqlen_q > seqlen_k) return FA_ERR_INVALID_ARG;
+  if (seqlen_q > fa::kDecodeMaxQ) return FA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (num_splits > (seqlen_k + 63) / 64) return FA_ERR_INVALID_ARG;
+  if ((long long)batch * seqlen_k * heads * head_dim > INT32_MAX * 8LL) return FA_ERR_INVALID_ARG;
+  int splits = 0, split_len = 0;
+  fa::decode_splits(batch, heads, seqlen_k, num_splits, &splits, &split_len);
+  const long long items = (long long)batch * heads * splits;
+  if (items > INT32_MAX || (long long)batch * heads * seqlen_q > INT32_MAX) return FA_ERR_INVALID_ARG;
+  const size_t part_o = (size_t)items * seqlen_q * head_dim * sizeof(float);
+  const size_t part_lse = (size_t)items * seqlen_q * sizeof(float);
+  *need = ((part_o + part_lse + 255) / 256) * 256;
+  pr.batch = batch;
+  pr.heads = heads;
+  pr.seqlen_q = seqlen_q;
+  pr.seqlen_k = seqlen_k;
+  pr.head_dim = head_dim;
+  pr.num_splits = splits;
+  pr.split_len = split_len;
+  pr.scale = scale;
+  pr.causal = causal != 0;
+  return FA_OK;
+}
+
 }  // namespace
 
 #define FA_EXPORT __attribute__((visibility("default")))
@@ -176,6 +208,39 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   if (r != FA_OK) return r;
   return fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen, head_dim,
                    softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+}
+
+FA_EXPORT size_t fa_fwd_decode_workspace_bytes(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+                                               int num_splits) {
+  fa::DecodeProblem pr{};
+  size_t need = 0;
+  if (check_decode(batch, heads, seqlen_q, seqlen_k, head_dim, 1.f, 0, num_splits, FA_DTYPE_BF16, pr, &need) != FA_OK)
+    return 0;
+  return need;
+}
+
+FA_EXPORT int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
+                            int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                            int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse)) return FA_ERR_INVALID_ARG;
+  fa::DecodeProblem pr{};
+  size_t need = 0;
+  const int st = check_decode(batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal, num_splits, dtype,
+                              pr, &need);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FA_ERR_WORKSPACE;
+  const size_t items = (size_t)batch * heads * pr.num_splits;
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.o = o;
+  pr.lse = lse;
+  pr.part_o = static_cast<float*>(workspace);
+  pr.part_lse = pr.part_o + items * seqlen_q * head_dim;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(fa::launch_decode_bf16(pr));
 }
 
 FA_EXPORT const char* fa_strerror(int status) {

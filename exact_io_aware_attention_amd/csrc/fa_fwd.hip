@@ -419,6 +419,175 @@ __global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd
   }
 }
 
+// ------------------------------------------------------------------------ decode
+//
+// Few new queries (seqlen_q <= 32, one MFMA column block) against a long key cache:
+// the work is reading K and V once, so the key range is cut into splits and each split
+// is one single-wave workgroup (two per compute unit, each with its own double-buffered
+// LDS tiles), which runs the forward tile loop over its keys for all the queries at
+// once. Each split leaves its O (normalised by its own sum, fp32) and logsumexp; a
+// second kernel merges them with weights exp(lse_s - lse) ("Softmax en línea" in the AI
+// Atlas summary: softmax blocks combine exactly through their maxima and sums). Causal
+// masking is bottom-right aligned: query i is at position seqlen_k - seqlen_q + i.
+struct DecParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  u16* o;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int B, H, Nq, Nk, n_splits, split_len;
+  float scale;
+  float c;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
+  constexpr int BC = kFwdBC, NB = D / 32, NS = D / 16;
+  using L = FwdLds<D>;
+  __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
+  const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
+  const int split = blockIdx.x % p.n_splits, bh = blockIdx.x / p.n_splits;
+  const int b = bh / p.H, h = bh % p.H;
+  const int ks = split * p.split_len;
+  const int ke = min(ks + p.split_len, p.Nk);  // the split sizing keeps ks < ke
+  const int qpos0 = p.Nk - p.Nq;                // position of query 0 in the sequence
+  const size_t stride = (size_t)p.H * D;
+  const u16* __restrict__ Qg = p.q + ((size_t)b * p.Nq * p.H + h) * D;
+  const u16* __restrict__ Kg = p.k + ((size_t)b * p.Nk * p.H + h) * D + (size_t)ks * stride;
+  const u16* __restrict__ Vg = p.v + ((size_t)b * p.Nk * p.H + h) * D + (size_t)ks * stride;
+  const int len = ke - ks;  // keys of this split, rows 0..len-1 of Kg / Vg
+
+  FwdState<D, 1> st;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    st.qf[0][s] = lr < p.Nq ? ld16(Qg + (size_t)lr * stride + 16 * s + 8 * g) : zero_bf16x8();
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) st.oacc[0][bb] = f32x16{};
+  st.m_run[0] = -INFINITY;
+  st.l_run[0] = 0.f;
+
+  TileDma<BC, D, L::KP, 1> kdma;
+  TileDma<BC, D, L::VP, 1> vdma;
+  // The wave index (0) is read from the hardware rather than written as a constant: with
+  // a literal the LDS destinations fold into constant address-space casts that this
+  // compiler's instruction selection rejects.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  kdma.init(stride, w, lane);
+  vdma.init(stride, w, lane);
+  const int n_kt = (len + BC - 1) / BC;
+  // The tile loop works in split-relative key indices; a query's position relative to
+  // the split is qpos0 + i - ks.
+  const int wq0 = qpos0 - ks;
+  auto step = [&](int kt, const u16* buf) {
+    const int k0 = kt * BC;
+    const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);  // wave-uniform
+    fwd_tile<D, 1, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
+  };
+  kdma.issue(buf0, Kg, 0, len, stride, w, lane);
+  vdma.issue(buf0 + L::KSZ, Vg, 0, len, stride, w, lane);
+  wait_vmem();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    // One wave: its LDS reads of a buffer are consumed by its MFMAs before the next
+    // copy into that buffer is issued, and its own copies are awaited with vmcnt.
+    if (kt + 1 < n_kt) {
+      kdma.issue(buf1, Kg, (kt + 1) * BC, len, stride, w, lane);
+      vdma.issue(buf1 + L::KSZ, Vg, (kt + 1) * BC, len, stride, w, lane);
+    }
+    step(kt, buf0);
+    wait_vmem();
+    if (kt + 1 >= n_kt) break;
+    if (kt + 2 < n_kt) {
+      kdma.issue(buf0, Kg, (kt + 2) * BC, len, stride, w, lane);
+      vdma.issue(buf0 + L::KSZ, Vg, (kt + 2) * BC, len, stride, w, lane);
+    }
+    step(kt + 1, buf1);
+    wait_vmem();
+  }
+
+  const float l_tot = pair_sum(st.l_run[0]);
+  if (lr >= p.Nq) return;
+  // A split can hold no key a query sees (causal): its weight in the merge is then 0.
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  float* __restrict__ Po = p.part_o + (((size_t)bh * p.n_splits + split) * p.Nq + lr) * D;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
+      *reinterpret_cast<f32x4*>(Po + 32 * bb + 8 * a + 4 * g) =
+          f32x4{st.oacc[0][bb][4 * a] * inv, st.oacc[0][bb][4 * a + 1] * inv, st.oacc[0][bb][4 * a + 2] * inv,
+                st.oacc[0][bb][4 * a + 3] * inv};
+    }
+  }
+  if (g == 0)
+    p.part_lse[((size_t)bh * p.n_splits + split) * p.Nq + lr] =
+        empty ? -INFINITY : st.m_run[0] * p.scale + logf(l_tot);
+}
+
+// One wave per (sequence, head, query): lse = log sum_s exp(lse_s), O = sum_s
+// exp(lse_s - lse) O_s, each lane owning head-dim entries lane and lane + 64.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecParams p) {
+  constexpr int NJ = D / 64;
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x % p.Nq, bh = blockIdx.x / p.Nq;
+  const int b = bh / p.H, h = bh % p.H;
+  const float* pl = p.part_lse + (size_t)bh * p.n_splits * p.Nq + i;
+  const float* po = p.part_o + ((size_t)bh * p.n_splits * p.Nq + i) * D;
+  float m = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) m = fmaxf(m, pl[(size_t)s * p.Nq]);
+  float den = 0.f, acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float wgt = expf(pl[(size_t)s * p.Nq] - m);
+      den += wgt;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = fmaf(wgt, po[(size_t)s * p.Nq * D + lane + 64 * j], acc[j]);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  u16* __restrict__ Og = p.o + (((size_t)b * p.Nq + i) * p.H + h) * D;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const __bf16 x = (__bf16)(acc[j] * inv);
+    Og[lane + 64 * j] = __builtin_bit_cast(u16, x);
+  }
+  if (lane == 0) p.lse[((size_t)b * p.H + h) * p.Nq + i] = den > 0.f ? m + logf(den) : -INFINITY;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_decode_t(const DecodeProblem& pr) {
+  DecParams p;
+  p.q = static_cast<const u16*>(pr.q);
+  p.k = static_cast<const u16*>(pr.k);
+  p.v = static_cast<const u16*>(pr.v);
+  p.o = static_cast<u16*>(pr.o);
+  p.lse = pr.lse;
+  p.part_o = pr.part_o;
+  p.part_lse = pr.part_lse;
+  p.B = pr.batch;
+  p.H = pr.heads;
+  p.Nq = pr.seqlen_q;
+  p.Nk = pr.seqlen_k;
+  p.n_splits = pr.num_splits;
+  p.split_len = pr.split_len;
+  p.scale = pr.scale;
+  p.c = pr.scale * kLog2e;
+  const unsigned bh = (unsigned)(pr.batch * pr.heads);
+  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3(bh * (unsigned)pr.num_splits), dim3(64), 0, pr.stream,
+                     p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(bh * (unsigned)pr.seqlen_q), dim3(64), 0, pr.stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_fwd_t(const Problem& pr) {
   // Two query blocks per wave halve the LDS reads per MFMA; at head_dim 128 their
@@ -448,5 +617,10 @@ hipError_t launch_fwd_t(const Problem& pr) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const Problem& p) { FA_DISPATCH(launch_fwd_t, p); }
+
+hipError_t launch_decode_bf16(const DecodeProblem& p) {
+  if (p.head_dim == 64) return p.causal ? launch_decode_t<64, true>(p) : launch_decode_t<64, false>(p);
+  return p.causal ? launch_decode_t<128, true>(p) : launch_decode_t<128, false>(p);
+}
 
 }  // namespace fa

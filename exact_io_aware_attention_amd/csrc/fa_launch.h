@@ -37,6 +37,44 @@ hipError_t launch_bwd_dq_bf16(const Problem& p);
 hipError_t launch_bwd_dkdv_fp32(const Problem& p);
 hipError_t launch_bwd_dq_fp32(const Problem& p);
 
+// Decoding: seqlen_q (1..32) new queries against seqlen_k cached keys, the key range cut
+// into num_splits splits of split_len keys (a multiple of 64) whose partial results
+// (O normalised by its own sum, fp32, and the split's logsumexp) go to the workspace and
+// are merged by logsumexp weights.
+struct DecodeProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;    // (batch, heads, num_splits, seqlen_q, head_dim)
+  float* part_lse;  // (batch, heads, num_splits, seqlen_q)
+  int batch, heads, seqlen_q, seqlen_k, head_dim;
+  int num_splits, split_len;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+constexpr int kDecodeMaxQ = 32;
+
+// Number of key splits and their length for a decode launch: `requested` (> 0) or, with
+// 0, enough splits for about 1024 single-wave workgroups, each at least 256 keys long.
+inline void decode_splits(int batch, int heads, int seqlen_k, int requested, int* num_splits, int* split_len) {
+  const long long bh = (long long)batch * heads;
+  long long want = requested > 0 ? requested : (1024 + bh - 1) / bh;
+  const long long max_by_len = requested > 0 ? (seqlen_k + 63) / 64 : (seqlen_k + 255) / 256;
+  if (want > max_by_len) want = max_by_len;
+  if (want < 1) want = 1;
+  long long len = (seqlen_k + want - 1) / want;
+  len = (len + 63) / 64 * 64;
+  *split_len = (int)len;
+  *num_splits = (int)((seqlen_k + len - 1) / len);
+}
+
+// Enqueues the split kernel and the merge kernel on p.stream.
+hipError_t launch_decode_bf16(const DecodeProblem& p);
+
 // Calls fn<head_dim, causal, varlen>(p) for the instantiation matching p.
 #define FA_DISPATCH(fn, p)                                                         \
   do {                                                                             \

@@ -140,6 +140,33 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
               float softmax_scale, int causal,
               const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
 
+/*
+ * Decoding: seqlen_q new queries (1..32) attend to a cache of seqlen_k keys and values
+ * of which they are the last seqlen_q positions (the pages cite faster inference; the
+ * semantics are the forward's with two lengths). q and o are (batch, seqlen_q, heads,
+ * head_dim), k and v (batch, seqlen_k, heads, head_dim); lse (batch, heads, seqlen_q).
+ * causal != 0: query i sees key j iff j <= seqlen_k - seqlen_q + i (bottom-right
+ * alignment; requires seqlen_q <= seqlen_k). bf16 only.
+ *
+ * The key range is cut into num_splits splits (0 = chosen by the library; otherwise at
+ * most ceil(seqlen_k / 64), and fewer may be used since a split is a whole number of
+ * 64-key tiles); each is processed independently into the workspace (its O
+ * normalised by its own softmax sum, and its logsumexp), then the splits are merged
+ * exactly by logsumexp weights ("Softmax en línea": softmax blocks combine through their
+ * maxima and sums). Two kernels run on `stream`.
+ *
+ * fa_fwd_decode_workspace_bytes returns the workspace size for these arguments (the same
+ * split choice fa_fwd_decode makes), or 0 if they are invalid. The workspace must be
+ * 256-byte aligned and at least that large; its contents on entry do not matter.
+ */
+size_t fa_fwd_decode_workspace_bytes(int batch, int heads, int seqlen_q, int seqlen_k,
+                                     int head_dim, int num_splits);
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+                  float softmax_scale, int causal, int num_splits,
+                  void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess",
-                                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_strerror"]
+                                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
+                                    "fa_fwd_decode_workspace_bytes", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -147,3 +148,51 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "libfa.so"))
     with pytest.raises(RuntimeError, match="not found"):
         fa.load_library()
+
+
+# ---------------------------------------------------------------- decode
+
+def _dec(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, batch=1, heads=2, seqlen_q=4, seqlen_k=1000, head_dim=128,
+                softmax_scale=0.1, causal=1, num_splits=0, workspace=None, workspace_bytes=0,
+                dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_decode(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen_q=33), fa.FA_ERR_UNSUPPORTED),
+    (dict(seqlen_q=8, seqlen_k=4, causal=1), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=17), fa.FA_ERR_INVALID_ARG),  # more splits than 64-key chunks
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(), fa.FA_ERR_WORKSPACE),                                   # no workspace
+    (dict(workspace=A, workspace_bytes=16), fa.FA_ERR_WORKSPACE),    # too small
+    (dict(workspace=A + 16, workspace_bytes=1 << 30), fa.FA_ERR_WORKSPACE),  # not 256-aligned
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    _lib()
+    assert _dec(**kw) == code
+
+
+def test_decode_workspace_size():
+    _lib()
+    # 1024 / (B*H) splits, each at least 256 keys: B*H = 256 -> 4 splits of 4096 keys
+    assert fa.fa_fwd_decode_workspace_bytes(8, 32, 1, 16384, 128, 0) == 256 * 4 * 1 * (128 + 1) * 4 // 256 * 256 + \
+        (256 if (256 * 4 * 129 * 4) % 256 else 0)
+    # explicit split count: 4 splits of 64 keys (256 keys), 5 queries, d = 64
+    want = 2 * 3 * 4 * 5 * (64 + 1) * 4
+    assert fa.fa_fwd_decode_workspace_bytes(2, 3, 5, 256, 64, 4) == (want + 255) // 256 * 256
+    # splits are whole multiples of 64 keys: 3 requested over 200 keys gives 2 of 128
+    want = 2 * 3 * 2 * 5 * (64 + 1) * 4
+    assert fa.fa_fwd_decode_workspace_bytes(2, 3, 5, 200, 64, 3) == (want + 255) // 256 * 256
+    assert fa.fa_fwd_decode_workspace_bytes(1, 1, 33, 100, 128, 0) == 0   # unsupported
+    assert fa.fa_fwd_decode_workspace_bytes(1, 1, 1, 100, 128, 3) == 0    # > ceil(100 / 64) splits

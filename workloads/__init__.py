@@ -33,6 +33,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "get", "make_inputs", "varlen_lengths",
     "cu_seqlens_from_lengths", "sample_rows", "Inputs",
+    "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs",
 ]
 
 
@@ -167,3 +168,53 @@ def make_inputs(w: Workload, seed: Optional[int] = None, *, batch: Optional[int]
         T = B * N
     q, k, v, do = (_randn(shape, seed + i, w.std, dt) for i in range(4))
     return Inputs(w, q, k, v, do, cu, list(lengths) if lengths is not None else None, B, N, T)
+
+
+# ---------------------------------------------------------------- decoding
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """seqlen_q new queries against a cache of seqlen_k keys and values (the last
+    seqlen_q positions of the sequence)."""
+    name: str
+    batch: int
+    heads: int
+    seqlen_q: int
+    seqlen_k: int
+    head_dim: int
+    causal: bool
+    std: float
+    seed: int
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# Synthetic stand-ins for generation with a long key cache (the pages cite faster
+# inference without a shape): one new token, and a 16-token chunk (speculative or
+# chunked decoding), against 16384 cached positions, Llama-shaped heads.
+DECODE_WORKLOADS = {
+    "d1": DecodeWorkload("d1", 8, 32, 1, 16384, 128, True, 1.0, 2001,
+                         description="decode: 1 query against a 16384-key cache"),
+    "d2": DecodeWorkload("d2", 8, 32, 16, 16384, 128, True, 1.0, 2002,
+                         description="decode: 16 queries against a 16384-key cache"),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None, *, batch: Optional[int] = None,
+                       seqlen_q: Optional[int] = None, seqlen_k: Optional[int] = None,
+                       heads: Optional[int] = None, head_dim: Optional[int] = None):
+    """Seeded bf16 Q (B, Nq, H, d), K and V (B, Nk, H, d) on the CPU, drawn like
+    ``make_inputs`` (tensor i from a generator seeded seed + i)."""
+    seed = w.seed if seed is None else seed
+    B = w.batch if batch is None else batch
+    Nq = w.seqlen_q if seqlen_q is None else seqlen_q
+    Nk = w.seqlen_k if seqlen_k is None else seqlen_k
+    H = w.heads if heads is None else heads
+    d = w.head_dim if head_dim is None else head_dim
+    q = _randn((B, Nq, H, d), seed, w.std, torch.bfloat16)
+    k = _randn((B, Nk, H, d), seed + 1, w.std, torch.bfloat16)
+    v = _randn((B, Nk, H, d), seed + 2, w.std, torch.bfloat16)
+    return q, k, v
