@@ -143,6 +143,51 @@ def standard_attention(q, k, v, do, scale: float, causal: bool, reps: int = 3):
     return {"fwd_ms": med(tf), "bwd_ms": med(tb), "peak_extra_bytes": int(peak)}, o.permute(0, 2, 1, 3)
 
 
+def decode_bench(reps: int = 20):
+    """fa_fwd_decode on the decode workloads: median time of `reps` calls (HIP events on
+    the launch stream) and the achieved rate of the algorithmic bytes (K and V read
+    once, Q read, O and LSE written) against the HBM peak."""
+    import torch
+    import exact_io_aware_attention_amd as fa
+    import workloads as W
+    res = {}
+    for name, w in sorted(W.DECODE_WORKLOADS.items()):
+        q, k, v = (t.cuda() for t in W.make_decode_inputs(w))
+        B, Nq, H, d = q.shape
+        Nk = k.shape[1]
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+        ws_bytes = fa.fa_fwd_decode_workspace_bytes(B, H, Nq, Nk, d, 0)
+        ws = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+        sp = torch.cuda.current_stream().cuda_stream
+
+        def call():
+            st = fa.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                                  Nk, d, w.scale, int(w.causal), 0, ws.data_ptr(), ws_bytes, fa.FA_DTYPE_BF16, sp)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_fwd_decode")
+
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        algo = 2 * B * Nk * H * d * 2 + 2 * B * Nq * H * d * 2 + B * H * Nq * 4
+        gbs = algo / (ms * 1e-3) / 1e9
+        res[name] = {"workload": w.description, "batch": B, "heads": H, "seqlen_q": Nq, "seqlen_k": Nk,
+                     "head_dim": d, "causal": w.causal, "ms": round(ms, 4), "algorithmic_bytes": algo,
+                     "achieved_gbs": round(gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS,
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm"}
+        del q, k, v, o, lse, ws
+    return res
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """Time the oracle (fp64, NumPy) on whole heads of the workload until ~budget_s."""
     import numpy as np
@@ -188,6 +233,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (not varlen)")
     ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (not varlen)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-attention comparison (materialised N x N scores)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -352,6 +398,9 @@ def main(argv=None) -> int:
         }
         del o_std
         torch.cuda.empty_cache()
+    if not a.no_decode:
+        log("bench: decode workloads")
+        out["decode"] = decode_bench()
     if a.cpu_budget > 0 and w.varlen is False:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)
