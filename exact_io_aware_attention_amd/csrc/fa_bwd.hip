@@ -113,9 +113,12 @@ constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
 // 64, since the first tile of each key range is partly above the diagonal and a larger
 // tile wastes more there (a per-block skip would break the interleaving of blocks).
 template <bool CAUSAL> constexpr int kv_bq() { return CAUSAL ? 64 : 128; }
+// LDS buffers in the query-tile pipeline: with three, the copies of the next two tiles
+// are in flight while one is used (64-query tiles fit three times in LDS, 128 twice).
+template <int BQ> constexpr int kv_stages() { return BQ == 64 ? 3 : 2; }
 
-// One double-buffered half: Q and dO tiles (row-major; read both row-wise for S and
-// dP and through transpose reads for dK and dV), then LSE*log2(e) and D per query.
+// One LDS buffer: Q and dO tiles (row-major; read both row-wise for S and dP and through
+// transpose reads for dK and dV), then LSE and D per query (all copied in by DMA).
 template <int D, int BQ>
 struct KvLds {
   static constexpr int P = pitch_both<D>();
@@ -196,7 +199,7 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
       const int qrow = 32 * a + 8 * r4 + 4 * g;  // registers 4r4..4r4+3: queries qrow..qrow+3
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + qrow);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], c, -l4[e]));
+      for (int e = 0; e < 4; ++e) sacc[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], c, -l4[e] * kLog2e));
     }
     if (mask) {  // wave-uniform: a diagonal or tail tile; hide keys after their query
 #pragma unroll
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   using L = KvLds<D, BQ>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
+  __shared__ __attribute__((aligned(16))) u16 buf2[kv_stages<BQ>() == 3 ? L::BUF : 8];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -279,23 +283,26 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
 
   TileDma<BQ, D, L::P, kKvWaves> tdma;
   tdma.init(stride, w, lane);
-  float lse_r = 0.f, dd_r = 0.f;  // this thread's share of the next tile's statistics
+  // Every wave issues the same number of copies per tile (its share of the Q and dO
+  // tiles, and one 64-row statistics copy: waves 0, 2 copy LSE, waves 1, 3 D; the
+  // duplicates land the same bytes), so a wave can wait for "all but the newest tile"
+  // with one vmcnt.
+  static_assert(BQ % 64 == 0 && kKvWaves == 4, "statistics copies assume 64-row pieces and 4 waves");
+  constexpr int CNT = 2 * TileDma<BQ, D, L::P, kKvWaves>::PER_WAVE + BQ / 64;
   auto issue = [&](int qt, u16* buf) {
     const int q0 = qt * BQ;
     tdma.issue(buf, Qg, q0, len, stride, w, lane);
     tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
-    if (tid < BQ) {
-      const int qq = min(q0 + tid, len - 1);  // rows past the end are masked in the tile
-      lse_r = p.lse[stat_index<VARLEN>(p, b, h, start, qq)] * kLog2e;
-      dd_r = p.dvec[stat_index<VARLEN>(p, b, h, start, qq)];
+#if __HIP_DEVICE_COMPILE__
+    const float* src = (w & 1) ? p.dvec : p.lse;
+    float* dst = reinterpret_cast<float*>(buf + L::STAT) + ((w & 1) ? BQ : 0);
+#pragma unroll
+    for (int j = 0; j < BQ / 64; ++j) {
+      const int qq = min(q0 + 64 * j + lane, len - 1);  // rows past the end are masked in the tile
+      __builtin_amdgcn_global_load_lds(src + stat_index<VARLEN>(p, b, h, start, qq),
+                                       (__attribute__((address_space(3))) void*)(dst + 64 * j), 4, 0, 0);
     }
-  };
-  auto finish = [&](u16* buf) {  // after the math: the statistics' loads have landed
-    if (tid < BQ) {
-      float* st_ = reinterpret_cast<float*>(buf + L::STAT);
-      st_[tid] = lse_r;
-      st_[BQ + tid] = dd_r;
-    }
+#endif
   };
   auto compute = [&](int qt, const u16* buf) {
     const int q0 = qt * BQ;
@@ -305,24 +312,51 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
       dkdv_tile<D, CAUSAL>(st, buf, q0, kj, len, mask, lane, p.c);
     }
   };
-  // Two LDS buffers in turn: the copy of the next query tile is in flight while the
-  // current one is used.
-  issue(qt_begin, buf0);
-  finish(buf0);
-  wait_vmem();
-  __syncthreads();
-  for (int qt = qt_begin; qt < n_qt; qt += 2) {
-    if (qt + 1 < n_qt) issue(qt + 1, buf1);
-    compute(qt, buf0);
-    if (qt + 1 < n_qt) finish(buf1);
+  if constexpr (kv_stages<BQ>() == 3) {
+    // Three LDS buffers in turn. Stage t: wait until tile t has landed (tile t+1 may
+    // still be in flight), barrier (every wave is past tile t-1 too), refill tile t-1's
+    // buffer with tile t+2, compute tile t.
+    auto wait_for = [&](int qt) {
+      if (qt + 1 < n_qt)
+        wait_vmem_count<CNT>();
+      else
+        wait_vmem();
+    };
+    issue(qt_begin, buf0);
+    if (qt_begin + 1 < n_qt) issue(qt_begin + 1, buf1);
+    for (int qt = qt_begin; qt < n_qt; qt += 3) {
+      wait_for(qt);
+      __syncthreads();
+      if (qt + 2 < n_qt) issue(qt + 2, buf2);
+      compute(qt, buf0);
+      if (qt + 1 >= n_qt) break;
+      wait_for(qt + 1);
+      __syncthreads();
+      if (qt + 3 < n_qt) issue(qt + 3, buf0);
+      compute(qt + 1, buf1);
+      if (qt + 2 >= n_qt) break;
+      wait_for(qt + 2);
+      __syncthreads();
+      if (qt + 4 < n_qt) issue(qt + 4, buf1);
+      compute(qt + 2, buf2);
+    }
+  } else {
+    // Two LDS buffers in turn: the copy of the next query tile is in flight while the
+    // current one is used.
+    issue(qt_begin, buf0);
     wait_vmem();
     __syncthreads();
-    if (qt + 1 >= n_qt) break;
-    if (qt + 2 < n_qt) issue(qt + 2, buf0);
-    compute(qt + 1, buf1);
-    if (qt + 2 < n_qt) finish(buf0);
-    wait_vmem();
-    __syncthreads();
+    for (int qt = qt_begin; qt < n_qt; qt += 2) {
+      if (qt + 1 < n_qt) issue(qt + 1, buf1);
+      compute(qt, buf0);
+      wait_vmem();
+      __syncthreads();
+      if (qt + 1 >= n_qt) break;
+      if (qt + 2 < n_qt) issue(qt + 2, buf0);
+      compute(qt + 1, buf1);
+      wait_vmem();
+      __syncthreads();
+    }
   }
 
 #pragma unroll

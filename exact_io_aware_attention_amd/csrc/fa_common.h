@@ -229,4 +229,12 @@ struct TileDma {
 // Wait for this wave's outstanding global loads (including LDS DMA) to land.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's global loads are outstanding (they complete in
+// issue order, so everything issued before the newest N has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmem_count() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace fa
