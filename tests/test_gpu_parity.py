@@ -126,3 +126,26 @@ def test_outputs_stay_in_bounds():
     for buf, fill in [(ob, -1000.0), (lb, -1000.0), (wsb, 0xA5)] + [(x[0], -1000.0) for x in grads]:
         edges = torch.cat([buf[:pad], buf[-pad:]]).float().cpu().numpy()
         assert np.all(edges == fill)
+
+
+def test_calls_run_on_the_given_stream():
+    """The library enqueues on the caller's stream: work on a side stream, ordered by
+    events only, gives the same result as on the default stream."""
+    import exact_io_aware_attention_amd as fa
+    w = W.get("c3")
+    inp = W.make_inputs(w, batch=1, seqlen=300, heads=2)
+    q, k, v, do = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.do))
+    o0, l0 = fa.forward(q, k, v, causal=True, softmax_scale=w.scale)
+    g0 = fa.backward(q, k, v, o0, l0, do, causal=True, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o1, l1 = fa.forward(q, k, v, causal=True, softmax_scale=w.scale, stream=side)
+        g1 = fa.backward(q, k, v, o1, l1, do, causal=True, softmax_scale=w.scale, stream=side)
+        done = torch.cuda.Event()
+        done.record(side)
+    done.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
