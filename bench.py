@@ -42,21 +42,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 753262813, "fetch_kib": 301250.3, "write_kib": 133122.5,
+    ("c3", "fwd"): {"bytes": 754627515, "fetch_kib": 301904.9, "write_kib": 133142.8,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 276875849, "fetch_kib": 131100.5, "write_kib": 8192.0,
+    ("c3", "bwd_preprocess"): {"bytes": 276877332, "fetch_kib": 131100.5, "write_kib": 8192.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 964630313, "fetch_kib": 337108.7, "write_kib": 267821.0,
+    ("c3", "bwd_dkdv"): {"bytes": 944048583, "fetch_kib": 328565.6, "write_kib": 264804.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 914367416, "fetch_kib": 378807.0, "write_kib": 135341.7,
+    ("c3", "bwd_dq"): {"bytes": 909685460, "fetch_kib": 376525.2, "write_kib": 135328.8,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5a42f5e1f6a6bec9b9dbb96db060c54a2e8be35ec9078e8b14bb4184e0439050",
+                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
