@@ -284,8 +284,8 @@ def main(argv=None) -> int:
                         w.scale, causal, cup, T, dt_code, sp), "fa_fwd")
 
     def k_pre():
-        check(fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d, cup, T,
-                                   dt_code, sp), "fa_bwd_preprocess")
+        check(fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N,
+                                   d, w.scale, cup, T, dt_code, sp), "fa_bwd_preprocess")
 
     def k_dkdv():
         check(fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),

@@ -57,7 +57,7 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
     lib.fa_bwd.restype = i32
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i32, i32, i32, i32, vp, i32, i32, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i32, i32, i32, i32, f32, vp, i32, i32, vp]
     lib.fa_bwd_preprocess.restype = i32
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
     lib.fa_bwd_dkdv.restype = i32
@@ -93,11 +93,11 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                                  cu_seqlens, total_tokens, dtype, stream)
 
 
-def fa_bwd_preprocess(o: int, dout: int, workspace: int, workspace_bytes: int, batch: int, heads: int,
-                      seqlen: int, head_dim: int, cu_seqlens: Optional[int], total_tokens: int, dtype: int,
-                      stream: Optional[int]) -> int:
-    return load_library().fa_bwd_preprocess(o, dout, workspace, workspace_bytes, batch, heads, seqlen,
-                                            head_dim, cu_seqlens, total_tokens, dtype, stream)
+def fa_bwd_preprocess(o: int, dout: int, lse: int, workspace: int, workspace_bytes: int, batch: int, heads: int,
+                      seqlen: int, head_dim: int, softmax_scale: float, cu_seqlens: Optional[int],
+                      total_tokens: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd_preprocess(o, dout, lse, workspace, workspace_bytes, batch, heads, seqlen,
+                                            head_dim, softmax_scale, cu_seqlens, total_tokens, dtype, stream)
 
 
 def fa_bwd_dkdv(q: int, k: int, v: int, dout: int, lse: int, workspace: int, workspace_bytes: int,

@@ -41,21 +41,24 @@ int check_common(int batch, int heads, int seqlen, int head_dim, float scale, in
   return FA_OK;
 }
 
-// D: one fp32 per (head, token), rounded up to 256 bytes.
-size_t workspace_bytes_for(int heads, long long tokens) {
+// D and -LSE / scale: one fp32 each per (head, token), each array rounded up to 256 bytes.
+size_t stat_bytes_for(int heads, long long tokens) {
   const size_t bytes = (size_t)heads * (size_t)tokens * sizeof(float);
   return ((bytes + 255) / 256) * 256;
 }
+size_t workspace_bytes_for(int heads, long long tokens) { return 2 * stat_bytes_for(heads, tokens); }
 
 // Checks shared by the backward entry points; sets pr.dvec to the workspace.
 int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
               int head_dim, float scale, int causal, const int32_t* cu_seqlens, int total_tokens, int dtype) {
   const int st = check_common(batch, heads, seqlen, head_dim, scale, causal, cu_seqlens, total_tokens, dtype, pr);
   if (st != FA_OK) return st;
+  if (scale == 0.f) return FA_ERR_INVALID_ARG;
   const size_t need = workspace_bytes_for(heads, pr.total_tokens);
   if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FA_ERR_WORKSPACE;
   pr.dvec = static_cast<float*>(workspace);
+  pr.mneg = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_bytes_for(heads, pr.total_tokens));
   return FA_OK;
 }
 
@@ -128,17 +131,19 @@ FA_EXPORT size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int he
 }
 
 
-FA_EXPORT int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int batch,
-                      int heads, int seqlen, int head_dim, const int32_t* cu_seqlens, int total_tokens,
-                      int dtype, void* stream) {
-  if (!o || !dout) return FA_ERR_INVALID_ARG;
-  if (!aligned(o) || !aligned(dout)) return FA_ERR_INVALID_ARG;
+FA_EXPORT int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
+                                size_t workspace_bytes, int batch, int heads, int seqlen, int head_dim,
+                                float softmax_scale, const int32_t* cu_seqlens, int total_tokens, int dtype,
+                                void* stream) {
+  if (!o || !dout || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(o) || !aligned(dout) || !aligned(lse)) return FA_ERR_INVALID_ARG;
   fa::Problem pr{};
-  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, 1.f, 0,
+  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale, 0,
                            cu_seqlens, total_tokens, dtype);
   if (st != FA_OK || pr.total_tokens == 0) return st;
   pr.o = o;
   pr.dout = dout;
+  pr.lse = lse;
   pr.stream = static_cast<hipStream_t>(stream);
   return status_of(fa::launch_bwd_pre(pr, dtype == FA_DTYPE_FP32));
 }
@@ -200,8 +205,8 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale,
                            causal, cu_seqlens, total_tokens, dtype);
   if (st != FA_OK || pr.total_tokens == 0) return st;
-  int r = fa_bwd_preprocess(o, dout, workspace, workspace_bytes, batch, heads, seqlen, head_dim, cu_seqlens,
-                            total_tokens, dtype, stream);
+  int r = fa_bwd_preprocess(o, dout, lse, workspace, workspace_bytes, batch, heads, seqlen, head_dim,
+                            softmax_scale, cu_seqlens, total_tokens, dtype, stream);
   if (r != FA_OK) return r;
   r = fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, batch, heads, seqlen, head_dim,
                   softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);

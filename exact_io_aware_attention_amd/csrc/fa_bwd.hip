@@ -4,7 +4,8 @@
 // the saved logsumexp, P = exp2(c * q.k - LSE * log2(e)) with c = scale * log2(e)
 // ("Recalcular en vez de guardar" in the AI Atlas summary of the FlashAttention paper).
 // Three kernels:
-//   bwd_pre   D_i = sum_k dO_ik * O_ik for every query row (fp32), from the stored O.
+//   bwd_pre   D_i = sum_k dO_ik * O_ik for every query row (fp32), from the stored O,
+//             and -LSE_i / scale, the starting value of the S accumulation in bwd_dkdv.
 //   bwd_dkdv  one workgroup per (sequence, head, 128-key tile); each wave owns 32 keys
 //             and keeps K, V fragments and the dK^T, dV^T accumulators in registers
 //             while it walks the 64-query tiles:
@@ -13,10 +14,15 @@
 //                 dV^T += dO^T P,  dK^T += Q^T dS
 //             S and dP are computed with one key per MFMA column, so P and dS feed the
 //             next products' B operands straight from registers; Q and dO are staged
-//             in LDS both row-major and transposed for the A operands.
+//             in LDS and read both row-wise and through transpose reads. At head_dim
+//             128 the 32-query blocks run in a software pipeline (the next block's S
+//             and dP on the matrix pipe while the vector ALUs do this block's softmax)
+//             over four LDS buffers; at 64 two waves share each SIMD instead.
 //   bwd_dq    the dQ accumulation pass: one workgroup per (sequence, head, 128-query
 //             tile), dQ^T += K^T dS^T over the key tiles, with one query per MFMA column.
 // There are no atomics, so the result is bitwise reproducible run to run.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -31,6 +37,7 @@ struct BwdParams {
   const u16* dout;
   const float* lse;
   const float* dvec;
+  const float* mneg;  // -LSE / scale (lse layout)
   float* dvec_out;
   u16* dq;
   u16* dk;
@@ -79,8 +86,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float* out) {
 // a contiguous span of O and dO.
 template <int D, typename T, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                      float* __restrict__ dvec, int H, int N, int T_total,
-                                                      long long rows) {
+                                                      const float* __restrict__ lse, float* __restrict__ dvec,
+                                                      float* __restrict__ mneg, float scale, int H, int N,
+                                                      int T_total, long long rows) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -101,6 +109,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
     const size_t idx = VARLEN ? (size_t)h * T_total + token
                               : ((size_t)(token / N) * H + h) * N + (size_t)(token % N);
     dvec[idx] = acc;
+    mneg[idx] = -lse[idx] / scale;
   }
 }
 
@@ -109,38 +118,58 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
-// Queries per tile: 128 halves the barriers and copies per query; under causal masking
-// 64, since the first tile of each key range is partly above the diagonal and a larger
-// tile wastes more there (a per-block skip would break the interleaving of blocks).
-template <bool CAUSAL> constexpr int kv_bq() { return CAUSAL ? 64 : 128; }
-// LDS buffers in the query-tile pipeline: with three, the copies of the next two tiles
-// are in flight while one is used (64-query tiles fit three times in LDS, 128 twice).
-template <int BQ> constexpr int kv_stages() { return BQ == 64 ? 3 : 2; }
+constexpr int kKvBQ = 64;             // queries per tile: two 32-query blocks
+constexpr int kKvPf = 3;              // operand reads run this many MFMA steps ahead
+// LDS buffers of the head_dim-128 kernel: four (two tiles in flight while one is read;
+// they fill the 160 KB).
+constexpr int kKvStages = 4;
 
-// One LDS buffer: Q and dO tiles (row-major; read both row-wise for S and dP and through
-// transpose reads for dK and dV), then LSE and D per query (all copied in by DMA).
-template <int D, int BQ>
+// One LDS buffer: Q and dO tiles (swizzled rows; read row-wise for S and dP and through
+// transpose reads for dK and dV), all copied in by DMA. The per-query statistics sit in
+// the pads of the Q tile: -LSE / scale of queries 16i .. 16i + 15 in the pad of row i,
+// D in the pad of row 4 + i (i = 0..3).
+template <int D>
 struct KvLds {
-  static constexpr int P = pitch_both<D>();
-  static constexpr int TSZ = BQ * P;               // elements of one tile
-  static constexpr int STAT = 2 * TSZ;             // u16 offset of the fp32 statistics
-  static constexpr int BUF = 2 * TSZ + 4 * BQ;     // + lse and D (2 x BQ floats)
+  static constexpr int P = swz_pitch<D>();
+  static constexpr int TSZ = kKvBQ * P;  // elements of one tile, pads included
+  static constexpr int BUF = 2 * TSZ;
+  // u16 element offset of the 16 statistics `which` (0: -LSE / scale, 1: D) of queries
+  // 16 i .. 16 i + 15
+  static constexpr int stat_pad(int which, int i) { return (4 * which + i) * P + D; }
 };
 
 template <int D>
 struct KvState {
   static constexpr int NB = D / 32, NS = D / 16;
-  bf16x8 kf[NS], vf[NS];  // this lane's key and value rows as B operands
-  f32x16 dvT[NB], dkT[NB];
+  bf16x8 kf[NS], vf[NS];    // this lane's key row and negated value row, as B operands
+  f32x16 dvT[NB], dkT[NB];  // dV^T and -dK^T
 };
 
-// One query tile for one wave, one 32-query block at a time (keeps the live score
-// registers to one block):
-//   S = Q K^T and dP = dO V^T with one key per column: register r of lane group g
-//   holds query q0 + 32a + crow_nat(r, g) against key kj;
-//   P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D);
-//   dV^T += dO^T P and dK^T += Q^T dS, whose A rows (head-dim entries) are read
-//   transposed from the row-major tiles with k-slots queries 16t + 4g + {0..3, 8..11}.
+// One 32-query block in flight, one key per C column: register r of lane group g holds
+// query q + crow_nat(r, g). The S product starts from -LSE / scale, so that
+// P = exp2(c s) with c = scale log2(e); with the value rows negated, the dP product
+// starts from D and yields D - dP. The softmax step turns s into P and dp into
+// P (D - dP) = -dS.
+struct KvBlock {
+  f32x16 s, dp;
+};
+
+// Statistics of the block at rows r0 of tile buffer buf, register set r4 (rows
+// q = r0 + 8 r4 + 4 g + 0..3, in the pad for queries 16 (q / 16) ..): -LSE / scale
+// (which = 0) or D (which = 1).
+template <int D>
+__device__ __forceinline__ f32x4 kv_stat4(const u16* buf, int which, int r0, int r4, int g) {
+  const u16* pad = buf + KvLds<D>::stat_pad(which, (r0 >> 4) + (r4 >> 1));
+  return *reinterpret_cast<const f32x4*>(pad + 16 * (r4 & 1) + 8 * g);
+}
+
+template <int D>
+__device__ __forceinline__ void kv_init_s(KvBlock& b, const u16* buf, int r0, int r4, int g) {
+  const f32x4 m4 = kv_stat4<D>(buf, 0, r0, r4, g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b.s[4 * r4 + e] = m4[e];
+}
+
 // dV^T / dK^T accumulation step. At head_dim 128 the accumulators (128 registers) are
 // pinned in AGPRs, leaving the VGPRs to the score arithmetic; at 64 they fit anyway.
 template <int D>
@@ -157,11 +186,375 @@ __device__ __forceinline__ void kv_acc_fence(f32x16& acc) {
   if constexpr (D == 128) agpr_acc_fence(acc);
 }
 
+// Row-wise operand j of the S / dP products of the block at rows r0 of tile buffer
+// `buf`: Q rows (slices 0 .. NS-1) for S, then dO rows for dP.
+template <int D>
+__device__ __forceinline__ bf16x8 kv_row_operand(const u16* buf, int r0, int j, int lane) {
+  constexpr int NS = D / 16;
+  return j < NS ? swz_row_operand<D>(buf, r0, j, lane)
+                : swz_row_operand<D>(buf + KvLds<D>::TSZ, r0, j - NS, lane);
+}
+
+// Transposed operand j of the dV / dK products of the block at rows r0: dO^T slices
+// (for dV^T += dO^T P), then Q^T slices (for dK^T += Q^T dS), k-slots in C-row order.
+template <int D>
+__device__ __forceinline__ bf16x8 kv_tr_operand(const u16* buf, int r0, int j, int lane) {
+  constexpr int NT = D / 16;  // operands per product
+  const int i = j % NT;
+  return swz_tr_operand<D>(j < NT ? buf + KvLds<D>::TSZ : buf, r0 + 16 * (i & 1), 32 * (i >> 1), lane);
+}
+
+// Softmax step for element r of block b (query qc + crow_nat(r, g)): P = exp2(c (S -
+// LSE / scale)), zero where masked, -dS = P (D - dP); every eighth element, eight of
+// each go to bf16 as half of a B operand.
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void kv_softmax_one(KvBlock& b, bf16x8 (&pb)[2], bf16x8 (&db)[2], int r, int qc, int kj,
+                                               int len, float c, int g) {
+  float e = fast_exp2(b.s[r] * c);
+  // Pin the exponential to this step (the compiler would otherwise sink the softmax
+  // towards its first use, out of the matrix-pipe phase it is meant to overlap).
+  asm volatile("" : "+v"(e));
+  if constexpr (MASK) {
+    const int qq = qc + crow_nat(r, g);
+    e = (qq >= len || (CAUSAL && kj > qq)) ? 0.f : e;
+  }
+  b.s[r] = e;
+  b.dp[r] *= e;
+  if (r % 8 == 7) {
+    pb[r / 8] = to_bf16x8(half_of(b.s, r / 8));
+    db[r / 8] = to_bf16x8(half_of(b.dp, r / 8));
+  }
+}
+
+// Phase X. The matrix pipe computes S and D - dP of block nx (rows rn of tile buffer
+// bn; when NXT) while the vector ALUs run the softmax step of block cu (query rows
+// qc.., tile buffer bc, rows rc; when CUR). rop holds the first kKvPf row operands of
+// nx and nx.s its starting value, read beforehand; D is read here into nx.dp; the last
+// steps read the first kKvPf transposed operands of phase Y for cu into top.
+template <int D, bool CAUSAL, bool NXT, bool CUR, bool MASK>
+__device__ __forceinline__ void kv_phase_x(const KvState<D>& st, KvBlock& nx, const u16* bn, int rn,
+                                           bf16x8 (&rop)[kKvPf], KvBlock& cu, bf16x8 (&pb)[2], bf16x8 (&db)[2],
+                                           const u16* bc, int rc, bf16x8 (&top)[kKvPf], int qc, int kj, int len,
+                                           float c, int lane) {
+  constexpr int NS = D / 16, NX = 2 * NS, EPS = 16 / NX;
+  const int g = lane >> 5;
+  if constexpr (NXT) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 d4 = kv_stat4<D>(bn, 1, rn, r4, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nx.dp[4 * r4 + e] = d4[e];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NX; ++j) {
+    if constexpr (NXT) {
+      const bf16x8 a = rop[j % kKvPf];
+      if (j + kKvPf < NX) rop[j % kKvPf] = kv_row_operand<D>(bn, rn, j + kKvPf, lane);
+      if (j < NS)
+        nx.s = mfma32(a, st.kf[j], nx.s);
+      else
+        nx.dp = mfma32(a, st.vf[j - NS], nx.dp);
+    }
+    if constexpr (CUR) {
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) kv_softmax_one<CAUSAL, MASK>(cu, pb, db, EPS * j + u, qc, kj, len, c, g);
+      if (j >= NX - kKvPf) top[j - (NX - kKvPf)] = kv_tr_operand<D>(bc, rc, j - (NX - kKvPf), lane);
+    }
+    step_fence();
+  }
+}
+
+// Phase Y for block cu (rows rc of tile buffer bc): dV^T += dO^T P, then
+// -dK^T += Q^T (-dS), with the transposed operands read kKvPf steps ahead (the first
+// ones in phase X). When NXT, the last steps read the first row operands and the
+// starting value of S of the block the next phase X computes (nx: rows rn of tile
+// buffer bn).
+template <int D, bool NXT>
+__device__ __forceinline__ void kv_phase_y(KvState<D>& st, const u16* bc, int rc, const bf16x8 (&pb)[2],
+                                           const bf16x8 (&db)[2], bf16x8 (&top)[kKvPf], const u16* bn, int rn,
+                                           bf16x8 (&rop)[kKvPf], KvBlock& nx, int lane) {
+  constexpr int NT = D / 16, NY = 2 * NT;
+  static_assert(NY >= 4 && NY >= kKvPf, "the prefetches need four steps");
+#pragma unroll
+  for (int j = 0; j < NY; ++j) {
+    const bf16x8 a = top[j % kKvPf];
+    if (j + kKvPf < NY) top[j % kKvPf] = kv_tr_operand<D>(bc, rc, j + kKvPf, lane);
+    const int i = j % NT;
+    if (j < NT)
+      kv_acc_mfma<D>(st.dvT[i >> 1], a, pb[i & 1]);
+    else
+      kv_acc_mfma<D>(st.dkT[i >> 1], a, db[i & 1]);
+    if constexpr (NXT) {
+      if (j >= NY - kKvPf) rop[j - (NY - kKvPf)] = kv_row_operand<D>(bn, rn, j - (NY - kKvPf), lane);
+      if (j >= NY - 4) kv_init_s<D>(nx, bn, rn, j - (NY - 4), lane >> 5);
+    }
+    step_fence();
+  }
+}
+
+// Phase X dispatch on the wave-uniform flags (each combination is its own straight-line
+// code).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0, int kj, int len, bool mask,
+__device__ __forceinline__ void kv_x(bool nxt, bool cur, bool mask, const KvState<D>& st, KvBlock& nx,
+                                     const u16* bn, int rn, bf16x8 (&rop)[kKvPf], KvBlock& cu, bf16x8 (&pb)[2],
+                                     bf16x8 (&db)[2], const u16* bc, int rc, bf16x8 (&top)[kKvPf], int qc, int kj,
+                                     int len, float c, int lane) {
+#define FA_KV_X(N, C, M) \
+  kv_phase_x<D, CAUSAL, N, C, M>(st, nx, bn, rn, rop, cu, pb, db, bc, rc, top, qc, kj, len, c, lane)
+  if (cur) {
+    if (nxt) {
+      if (mask) FA_KV_X(true, true, true); else FA_KV_X(true, true, false);
+    } else {
+      if (mask) FA_KV_X(false, true, true); else FA_KV_X(false, true, false);
+    }
+  } else if (nxt) {
+    FA_KV_X(true, false, false);
+  }
+#undef FA_KV_X
+}
+
+// One workgroup per (sequence, head, 128-key tile); wave w owns keys k0 + 32w .. + 31
+// and walks the 64-query tiles from the diagonal on, two 32-query blocks per tile, in a
+// software pipeline across blocks and tiles:
+//   X(t,0) [S, dP of (t,1) | softmax of (t,0)]  barrier  Y(t,0) [dV, dK of (t,0)]
+//   X(t,1) [S, dP of (t+1,0) | softmax of (t,1)]  Y(t,1) [dV, dK of (t,1)]
+// The barrier in tile t follows the wait for tile t+1 and precedes the copy of tile
+// t+3 into the buffer tile t-1 used; a wave's last read of tile t-1 (in Y(t-1,1))
+// comes before it.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "head_dim 64 has its own kernel (bwd_dkdv_rows_kernel)");
+  constexpr int BK = kKvBK, BQ = kKvBQ, NS = D / 16, NB = D / 32;
+  constexpr int S = kKvStages;
+  using L = KvLds<D>;
+  using Dma = TileDma<BQ, D, L::P, kKvWaves, true>;
+  __shared__ __attribute__((aligned(16))) u16 lds[S * L::BUF];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+
+  // Workgroup -> (sequence, head, key tile), head-grouped per XCD (the head's Q and dO
+  // stay in L2); under causal the first key tiles see the most queries and come first.
+  int bh, kt;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, false, true, bh, kt);
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int k0 = kt * BK;
+  if (k0 >= len) return;
+
+  const size_t stride = (size_t)p.H * D;
+  const size_t base = ((size_t)start * p.H + h) * D;
+  const u16* __restrict__ Qg = p.q + base;
+  const u16* __restrict__ dOg = p.dout + base;
+
+  const int wk0 = k0 + 32 * w;  // first key of this wave
+  const int kj = wk0 + lr;      // this lane's key
+
+  KvState<D> st;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const size_t off = base + (size_t)kj * stride + 16 * s + 8 * g;
+    st.kf[s] = kj < len ? ld16(p.k + off) : zero_bf16x8();
+    const bf16x8 v = kj < len ? ld16(p.v + off) : zero_bf16x8();
+    st.vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);
+  }
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    st.dvT[bb] = f32x16{};
+    st.dkT[bb] = f32x16{};
+  }
+
+  const int qt_begin = CAUSAL ? k0 / BQ : 0;
+  const int n_qt = (len + BQ - 1) / BQ;
+  // First tile this wave computes (wave-uniform): under causal the first one whose last
+  // query reaches the wave's first key; none when the wave's keys are all past the end.
+  const int qt_w = wk0 >= len ? n_qt : (CAUSAL ? max(qt_begin, wk0 / BQ) : 0);
+
+  Dma tdma;
+  tdma.init(stride, w, lane);
+  auto bufp = [&](int qt) -> u16* { return lds + ((unsigned)(qt - qt_begin) % S) * L::BUF; };
+  // Every wave issues the same number of copies per tile (its share of the Q and dO
+  // tiles, and two 16-query statistics copies: wave w copies -LSE / scale and D of
+  // queries 16w .. 16w + 15 into their pads), so a wave can wait for "all but the
+  // newest k tiles" with one vmcnt.
+  static_assert(BQ == 64 && kKvWaves == 4, "statistics copies assume 16 queries per wave");
+  constexpr int CNT = 2 * Dma::PER_WAVE + 2;
+  auto issue = [&](int qt) {
+    u16* buf = bufp(qt);
+    const int q0 = qt * BQ;
+    tdma.issue(buf, Qg, q0, len, stride, w, lane);
+    tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
+#if __HIP_DEVICE_COMPILE__
+    // lane 16w + t lands at dst + 4 (16w + t) bytes: dst = pad - 64w bytes puts it at pad + 4t
+    const int qq = min(q0 + lane, len - 1);  // rows past the end are masked in the tile
+    const size_t si = stat_index<VARLEN>(p, b, h, start, qq);
+    if ((lane >> 4) == w) {
+      dma_lds_b32(p.mneg + si, buf + L::stat_pad(0, w) - 32 * w);
+      dma_lds_b32(p.dvec + si, buf + L::stat_pad(1, w) - 32 * w);
+    }
+#endif
+  };
+  // Wait until the tiles issued after the wanted one (younger of them: 0 .. 2) are the
+  // only copies this wave still has in flight.
+  auto wait_tiles = [&](int younger) {
+    if (younger >= 2)
+      wait_vmem_count<2 * CNT>();
+    else if (younger == 1)
+      wait_vmem_count<CNT>();
+    else
+      wait_vmem();
+  };
+
+  // Prologue: tiles qt_begin .. qt_begin + S - 2 in flight; wait for the first.
+  static_assert(S == 3 || S == 4, "two or three tiles ahead");
+  issue(qt_begin);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    settle(st.kf[s]);
+    settle(st.vf[s]);
+  }
+  for (int i = 1; i < S - 1; ++i)
+    if (qt_begin + i < n_qt) issue(qt_begin + i);
+  wait_tiles(min(S - 2, n_qt - qt_begin - 1));
+  lds_barrier();
+
+  KvBlock blk0, blk1;
+  bf16x8 rop[kKvPf], top[kKvPf], pb[2], db[2];
+  // A wave's first block: S and D - dP alone, then the row operands of the next block.
+  auto first_block = [&](int qt) {
+    const u16* bf = bufp(qt);
+#pragma unroll
+    for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 0, j, lane);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) kv_init_s<D>(blk0, bf, 0, r4, g);
+    kv_phase_x<D, CAUSAL, true, false, false>(st, blk0, bf, 0, rop, blk1, pb, db, bf, 0, top, 0, kj, len, p.c,
+                                              lane);
+#pragma unroll
+    for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 32, j, lane);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) kv_init_s<D>(blk1, bf, 32, r4, g);
+  };
+  // The collective step between the two blocks of tile qt: wait for tile qt + 1 (tiles
+  // up to qt + S - 2 may still be in flight), barrier, then refill the buffer of tile
+  // qt - 1 with tile qt + S - 1.
+  auto next_tile_sync = [&](int qt) {
+    wait_tiles(max(0, min(S - 3, n_qt - qt - 2)));
+    lds_barrier();
+    if (qt + S - 1 < n_qt) issue(qt + S - 1);
+  };
+  auto mask_of = [&](int q0) { return q0 + BQ > len || (CAUSAL && q0 < wk0 + 31); };  // wave-uniform
+
+  // Tiles before this wave's first: only the collective part.
+  const int qs = min(qt_w, n_qt);
+  if (qs == qt_begin && qs < n_qt) first_block(qs);
+  for (int qt = qt_begin; qt < qs; ++qt) {
+    if (qt + 1 < n_qt) next_tile_sync(qt);
+    if (qt + 1 == qs && qs < n_qt) first_block(qs);
+  }
+  // Every tile but the last: the full pipeline. Each buffer slot has its own copy of
+  // the code, so that LDS addresses are per-lane offsets plus constants.
+  auto tile_step = [&](int qt) {
+    const u16* bc = bufp(qt);
+    const u16* bn = bufp(qt + 1);
+    const int q0 = qt * BQ;
+    const bool mask = mask_of(q0);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk1, bc, 32, rop, blk0, pb, db, bc, 0, top, q0, kj, len, p.c, lane);
+    next_tile_sync(qt);
+    kv_phase_y<D, true>(st, bc, 0, pb, db, top, bn, 0, rop, blk0, lane);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk0, bn, 0, rop, blk1, pb, db, bc, 32, top, q0 + 32, kj, len, p.c, lane);
+    kv_phase_y<D, true>(st, bc, 32, pb, db, top, bn, 32, rop, blk1, lane);
+  };
+  for (int qt = qs; qt < n_qt - 1; ++qt) tile_step(qt);
+  // The last tile.
+  if (qs < n_qt) {
+    const int qt = n_qt - 1;
+    const u16* bc = bufp(qt);
+    const int q0 = qt * BQ;
+    const bool mask = mask_of(q0);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk1, bc, 32, rop, blk0, pb, db, bc, 0, top, q0, kj, len, p.c, lane);
+    kv_phase_y<D, false>(st, bc, 0, pb, db, top, bc, 0, rop, blk0, lane);
+    kv_x<D, CAUSAL>(false, true, mask, st, blk0, bc, 0, rop, blk1, pb, db, bc, 32, top, q0 + 32, kj, len, p.c, lane);
+    kv_phase_y<D, false>(st, bc, 32, pb, db, top, bc, 32, rop, blk1, lane);
+  }
+
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    kv_acc_fence<D>(st.dvT[bb]);
+    kv_acc_fence<D>(st.dkT[bb]);
+  }
+  if (kj >= len) return;
+  u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
+  u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
+  const float nscale = -p.scale;  // the accumulator holds -dK^T / scale
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
+      const int col = 32 * bb + 8 * a + 4 * g;
+      store_bf16x4(dKg + col, st.dkT[bb][4 * a] * nscale, st.dkT[bb][4 * a + 1] * nscale,
+                   st.dkT[bb][4 * a + 2] * nscale, st.dkT[bb][4 * a + 3] * nscale);
+      store_bf16x4(dVg + col, st.dvT[bb][4 * a], st.dvT[bb][4 * a + 1], st.dvT[bb][4 * a + 2],
+                   st.dvT[bb][4 * a + 3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ bwd_dkdv, head_dim 64
+//
+// At head_dim 64 a block has half the matrix work of head_dim 128 against the same
+// softmax arithmetic, and the dK/dV state fits in 256 registers, so two waves share each
+// SIMD and overlap one another's vector and matrix work; this kernel does the blocks in
+// order, without the cross-block pipeline of the head_dim-128 kernel. Each wave owns
+// 32 keys; Q and dO tiles sit in LDS with padded rows (pitch_both), read row-wise for
+// S and dP and through transpose reads for dV and dK; LSE and D are copied per tile.
+
+// Queries per tile: 128 halves the barriers and copies per query; under causal masking
+// 64, since the first tile of each key range is partly above the diagonal and a larger
+// tile wastes more there (a per-block skip would break the interleaving of blocks).
+template <bool CAUSAL> constexpr int rk_bq() { return CAUSAL ? 64 : 128; }
+// LDS buffers in the query-tile pipeline: with three, the copies of the next two tiles
+// are in flight while one is used (64-query tiles fit three times in LDS, 128 twice).
+template <int BQ> constexpr int rk_stages() { return BQ == 64 ? 3 : 2; }
+
+// One LDS buffer: Q and dO tiles (row-major; read both row-wise for S and dP and through
+// transpose reads for dK and dV), then LSE and D per query (all copied in by DMA).
+template <int D, int BQ>
+struct RkLds {
+  static constexpr int P = pitch_both<D>();
+  static constexpr int TSZ = BQ * P;               // elements of one tile
+  static constexpr int STAT = 2 * TSZ;             // u16 offset of the fp32 statistics
+  static constexpr int BUF = 2 * TSZ + 4 * BQ;     // + lse and D (2 x BQ floats)
+};
+
+template <int D>
+struct RkState {
+  static constexpr int NB = D / 32, NS = D / 16;
+  bf16x8 kf[NS], vf[NS];  // this lane's key and value rows as B operands
+  f32x16 dvT[NB], dkT[NB];
+};
+
+// One query tile for one wave, one 32-query block at a time (keeps the live score
+// registers to one block):
+//   S = Q K^T and dP = dO V^T with one key per column: register r of lane group g
+//   holds query q0 + 32a + crow_nat(r, g) against key kj;
+//   P = exp2(c S - LSE log2e) (exact, normalised), dS = P (dP - D);
+//   dV^T += dO^T P and dK^T += Q^T dS, whose A rows (head-dim entries) are read
+//   transposed from the row-major tiles with k-slots queries 16t + 4g + {0..3, 8..11}.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void rk_tile(RkState<D>& st, const u16* buf, int q0, int kj, int len, bool mask,
                                           int lane, float c) {
-  constexpr int BQ = kv_bq<CAUSAL>();
-  using L = KvLds<D, BQ>;
+  constexpr int BQ = rk_bq<CAUSAL>();
+  using L = RkLds<D, BQ>;
   constexpr int NB = D / 32, NS = D / 16, NA = BQ / 32;
   constexpr int P = L::P;
   const u16* Qs = buf;
@@ -229,13 +622,13 @@ __device__ __forceinline__ void dkdv_tile(KvState<D>& st, const u16* buf, int q0
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
-  constexpr int BK = kKvBK, BQ = kv_bq<CAUSAL>(), NT = kKvThreads;
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_rows_kernel(BwdParams p) {
+  constexpr int BK = kKvBK, BQ = rk_bq<CAUSAL>(), NT = kKvThreads;
   constexpr int NB = D / 32, NS = D / 16;
-  using L = KvLds<D, BQ>;
+  using L = RkLds<D, BQ>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
-  __shared__ __attribute__((aligned(16))) u16 buf2[kv_stages<BQ>() == 3 ? L::BUF : 8];
+  __shared__ __attribute__((aligned(16))) u16 buf2[rk_stages<BQ>() == 3 ? L::BUF : 8];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -265,7 +658,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int wk0 = k0 + 32 * w;  // first key of this wave
   const int kj = wk0 + lr;      // this lane's key
 
-  KvState<D> st;
+  RkState<D> st;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const size_t off = base + (size_t)kj * stride + 16 * s + 8 * g;
@@ -299,8 +692,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
 #pragma unroll
     for (int j = 0; j < BQ / 64; ++j) {
       const int qq = min(q0 + 64 * j + lane, len - 1);  // rows past the end are masked in the tile
-      __builtin_amdgcn_global_load_lds(src + stat_index<VARLEN>(p, b, h, start, qq),
-                                       (__attribute__((address_space(3))) void*)(dst + 64 * j), 4, 0, 0);
+      dma_lds_b32(src + stat_index<VARLEN>(p, b, h, start, qq), dst + 64 * j);
     }
 #endif
   };
@@ -309,10 +701,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     // wave-uniform: skip tiles whose queries all precede this wave's keys
     if (wk0 < len && (!CAUSAL || q0 + BQ - 1 >= wk0)) {
       const bool mask = q0 + BQ > len || (CAUSAL && q0 < wk0 + 31);
-      dkdv_tile<D, CAUSAL>(st, buf, q0, kj, len, mask, lane, p.c);
+      rk_tile<D, CAUSAL>(st, buf, q0, kj, len, mask, lane, p.c);
     }
   };
-  if constexpr (kv_stages<BQ>() == 3) {
+  if constexpr (rk_stages<BQ>() == 3) {
     // Three LDS buffers in turn. Stage t: wait until tile t has landed (tile t+1 may
     // still be in flight), barrier (every wave is past tile t-1 too), refill tile t-1's
     // buffer with tile t+2, compute tile t.
@@ -323,6 +715,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
         wait_vmem();
     };
     issue(qt_begin, buf0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      settle(st.kf[s]);
+      settle(st.vf[s]);
+    }
     if (qt_begin + 1 < n_qt) issue(qt_begin + 1, buf1);
     for (int qt = qt_begin; qt < n_qt; qt += 3) {
       wait_for(qt);
@@ -344,6 +741,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     // Two LDS buffers in turn: the copy of the next query tile is in flight while the
     // current one is used.
     issue(qt_begin, buf0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      settle(st.kf[s]);
+      settle(st.vf[s]);
+    }
     wait_vmem();
     __syncthreads();
     for (int qt = qt_begin; qt < n_qt; qt += 2) {
@@ -522,6 +924,13 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
     }
   };
   issue(0, buf0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    settle(st.qf[s]);
+    settle(st.dof[s]);
+  }
+  settle(st.lse2);
+  settle(st.dd);
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
@@ -594,6 +1003,7 @@ BwdParams make_params(const Problem& pr) {
   p.dout = static_cast<const u16*>(pr.dout);
   p.lse = pr.lse;
   p.dvec = pr.dvec;
+  p.mneg = pr.mneg;
   p.dvec_out = pr.dvec;
   p.dq = static_cast<u16*>(pr.dq);
   p.dk = static_cast<u16*>(pr.dk);
@@ -616,12 +1026,12 @@ hipError_t launch_pre_t(const Problem& pr) {
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   if (pr.cu_seqlens)
     hipLaunchKernelGGL((bwd_pre_kernel<D, T, true>), grid, dim3(256), 0, pr.stream,
-                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.dvec, pr.heads,
-                       pr.seqlen, pr.total_tokens, rows);
+                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg,
+                       pr.scale, pr.heads, pr.seqlen, pr.total_tokens, rows);
   else
     hipLaunchKernelGGL((bwd_pre_kernel<D, T, false>), grid, dim3(256), 0, pr.stream,
-                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.dvec, pr.heads,
-                       pr.seqlen, pr.total_tokens, rows);
+                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg,
+                       pr.scale, pr.heads, pr.seqlen, pr.total_tokens, rows);
   return hipGetLastError();
 }
 
@@ -629,8 +1039,11 @@ template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dkdv_t(const Problem& pr) {
   BwdParams p = make_params(pr);
   p.n_tiles = (pr.seqlen + kKvBK - 1) / kKvBK;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>),
-                     dim3((unsigned)(p.n_tiles * pr.batch * pr.heads)), dim3(kKvThreads), 0, pr.stream, p);
+  const dim3 grid((unsigned)(p.n_tiles * pr.batch * pr.heads));
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((bwd_dkdv_rows_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
   return hipGetLastError();
 }
 

@@ -46,6 +46,10 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Closes one step of a software-pipelined phase: the scheduler moves no instruction
+// across it, so each step keeps the reads, MFMAs and vector work it was written with.
+__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Wait states between an MFMA writing `acc` and VALU / v_accvgpr_read reads of it.
 __device__ __forceinline__ void agpr_acc_fence(f32x16& acc) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
@@ -158,6 +162,58 @@ template <int D> constexpr int pitch_both() { return D == 64 ? D + 8 : D + 24; }
 __device__ __forceinline__ int crow_nat(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 // ---------------------------------------------------------------------------------------
+// Swizzled LDS tiles, for operands read both row-wise and through transpose reads: rows
+// of D + 32 bf16 (the D elements, then a 64-byte pad), with 16-byte chunk c of row r
+// stored at chunk position c ^ swz_j(r), swz_j(r) = (r >> 2) & 3. Counted in 16-byte
+// chunks, the 64 banks are 16 positions, and each row starts 4 (D = 128: 20 chunks per
+// row) or 12 (D = 64: 12 chunks) positions after the previous one. Hence
+//   row-wise operand reads, 16 lanes = one chunk of 16 consecutive rows (16-aligned):
+//     within each group of 4 rows the pitch puts the rows on distinct multiples of 4
+//     (bits 2-3), and across the 4 groups the XOR gives distinct low bits;
+//   transpose reads, 32 lanes = chunks 4m .. 4m + 3 of 4 consecutive rows (4-aligned):
+//     the pitch separates the rows (bits 2-3) and the XOR permutes within the 4 chunks;
+// so neither shape has bank conflicts. The XOR never leaves a group of 4 chunks, so data
+// stays out of the pads, which are free for other use. The pattern depends on r % 16
+// only: tiles whose first row is a multiple of 16 share it. Every address splits into a
+// per-lane part that does not depend on the row block or the slice, and a constant.
+// ---------------------------------------------------------------------------------------
+template <int D>
+constexpr int swz_pitch() {
+  static_assert(D == 64 || D == 128, "swizzled tiles are 64 or 128 elements wide");
+  return D + 32;
+}
+
+__device__ __forceinline__ int swz_j(int r) { return (r >> 2) & 3; }
+
+// Row-wise A or B operand from a swizzled tile: lane l reads row r0 + l % 32, elements
+// 16 s + 8 g .. + 7 (g = l / 32), i.e. chunk 2 s + g = 4 (s / 2) + (2 (s % 2) + g).
+// r0 must be a multiple of 16.
+template <int D>
+__device__ __forceinline__ bf16x8 swz_row_operand(const u16* t, int r0, int s, int lane) {
+  constexpr int P = swz_pitch<D>();
+  const int lr = lane & 31, g = lane >> 5;
+  const int lane_part = lr * P + 8 * (((2 * (s & 1)) | g) ^ swz_j(lr));
+  return *reinterpret_cast<const bf16x8*>(t + lane_part + r0 * P + 32 * (s >> 1));
+}
+
+// lds_tr_operand on a swizzled tile. r0 must be a multiple of 16 and c0 of 32.
+template <int D>
+__device__ __forceinline__ bf16x8 swz_tr_operand(const u16* t, int r0, int c0, int lane) {
+  constexpr int P = swz_pitch<D>();
+  const int i = lane & 15;
+  const int G = lane >> 4;
+  const int rl = 4 * (G >> 1) + (i >> 2);            // row within the 16-row group (lo read)
+  const int u = 2 * (G & 1) + ((i & 3) >> 1);        // chunk within the group of 4
+  const int e = 4 * (i & 1);                         // element within the chunk
+  const int lo = rl * P + 8 * (u ^ swz_j(rl)) + e;
+  const int hi = (rl + 8) * P + 8 * (u ^ swz_j(rl + 8)) + e;
+  const int cst = r0 * P + c0;                       // chunk group c0 / 32 starts at element c0
+  const i16x4 a = ds_read_tr16(t + lo + cst);
+  const i16x4 b = ds_read_tr16(t + hi + cst);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------------------------------
 // Global -> LDS tile staging. `src` points at row 0 of a matrix whose rows are
 // `stride` elements apart; rows [r0, r0 + ROWS) are staged and rows >= `len` are
 // zero-filled. All NT threads of the workgroup call these together.
@@ -170,9 +226,52 @@ __device__ __forceinline__ int crow_nat(int r, int g) { return 8 * (r >> 2) + 4 
 // (CPP = PITCH / 8 chunks per row); lanes that land on a padding chunk copy the row's
 // first chunk there, which is never read. Rows at or past `len` are clamped to row
 // len - 1: the data is finite and every consumer masks those rows out.
-template <int ROWS, int D, int PITCH, int NWAVES>
+// Global -> LDS copies (global_load_lds_dword / _dwordx4), written as inline asm. Lane i
+// of a wave lands its 4 or 16 bytes at LDS address dst + 4 i or dst + 16 i (dst, a
+// wave-uniform LDS address, goes to M0). Issued through the compiler builtin instead,
+// a copy counts as a pending LDS write that the compiler cannot tell apart from the
+// tiles being read: it then waits for every copy in flight (vmcnt(0)) before the next
+// LDS read, which undoes a multi-buffer pipeline. Callers wait for the copies
+// themselves (wait_vmem, wait_vmem_count) before a barrier that publishes the tile.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// (The s_nop is the wait state an M0 write needs before the copy reads it.)
+__device__ __forceinline__ void dma_lds_b128(const void* src, const void* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
+
+__device__ __forceinline__ void dma_lds_b32(const void* src, const void* dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
+
+// A use of x that makes the compiler wait here for the loads that produced it. The
+// compiler's own waits are vmcnt(0) (it does not count the asm copies above), so a
+// register loaded before a tile loop and first read inside it would cost a wait inside
+// the loop, on every trip, for every tile copy in flight. Called once, right after the
+// first tile's copy is issued, the wait overlaps that copy instead.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" : : "v"(x));
+}
+
+// Workgroup barrier without a memory fence: unlike __syncthreads it does not make the
+// compiler wait for outstanding copies; it only keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// With SWZ the tile is a swizzled one (PITCH == swz_pitch<D>()): each lane fetches the
+// chunk whose swizzled position is the slot it writes, and lanes on a pad chunk copy
+// nothing (the pads stay free).
+template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false>
 struct TileDma {
   static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
+  static_assert(!SWZ || (PITCH == D + 32 && ROWS % 16 == 0), "swizzled tiles: pitch D + 32, 16-row aligned");
   static constexpr int CPP = PITCH / 8;
   static constexpr int TOTAL = ROWS * CPP;
   static_assert(TOTAL % 64 == 0, "a tile must be a whole number of 64-chunk copies");
@@ -185,15 +284,26 @@ struct TileDma {
   // fewer repeats the last one (same bytes to the same place), which keeps the issue
   // free of branches.
   uint32_t off[PER_WAVE];
+  uint32_t pad_bits;  // SWZ: bit i set when this lane's chunk in copy i is a pad chunk
 
   __device__ __forceinline__ static int copy_index(int w, int i) { return min(w + i * NWAVES, NINST - 1); }
 
+  // Chunk of global row `row` that lands in chunk slot c of the LDS row.
+  __device__ __forceinline__ static int src_chunk(int row, int c) {
+    if constexpr (SWZ)
+      return c < D / 8 ? c ^ swz_j(row) : 0;
+    else
+      return c < D / 8 ? c : 0;
+  }
+
   __device__ __forceinline__ void init(size_t stride, int w, int lane) {
+    pad_bits = 0;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int L = 64 * copy_index(w, i) + lane;
       const int row = L / CPP, c = L % CPP;
-      off[i] = (uint32_t)(((size_t)row * stride + (c < D / 8 ? 8 * c : 0)) * sizeof(u16));
+      off[i] = (uint32_t)(((size_t)row * stride + 8 * src_chunk(row, c)) * sizeof(u16));
+      if (SWZ && c >= D / 8) pad_bits |= 1u << i;
     }
   }
 
@@ -208,9 +318,7 @@ struct TileDma {
       const char* base = reinterpret_cast<const char*>(src + (size_t)r0 * stride);
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds(base + off[i],
-                                         (__attribute__((address_space(3))) void*)(dst + 512 * copy_index(w, i)),
-                                         16, 0, 0);
+        if (!SWZ || !((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * copy_index(w, i));
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -218,8 +326,8 @@ struct TileDma {
         const int L = 64 * k + lane;
         const int row = L / CPP, c = L % CPP;
         const int grow = min(r0 + row, len - 1);
-        const u16* g = src + (size_t)grow * stride + (c < D / 8 ? 8 * c : 0);
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(dst + 512 * k), 16, 0, 0);
+        const u16* g = src + (size_t)grow * stride + 8 * src_chunk(row, c);
+        if (!SWZ || c < D / 8) dma_lds_b128(g, dst + 512 * k);
       }
     }
 #endif

@@ -74,9 +74,9 @@ struct FwdState {
 // exponentials of one block run while the matrix pipe works on the other:
 //   S_0 | S_1 with exp(S_0) | P_0 V_0 with exp(S_1) | P_1 V_1
 // In each phase, operand reads run kPf steps ahead of the MFMA that uses them, and a
-// scheduling barrier closes every step, so the compiler neither sinks a read next to
-// its use (exposing the LDS latency) nor hoists all of them (a register per read).
-__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+// scheduling barrier (step_fence) closes every step, so the compiler neither sinks a
+// read next to its use (exposing the LDS latency) nor hoists all of them (a register
+// per read).
 
 constexpr int kFwdPf = 3;
 
@@ -337,6 +337,10 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
   };
   // Two LDS buffers in turn: the copy of tile kt+1 is in flight while tile kt is used.
   issue(0, buf0);
+#pragma unroll
+  for (int n = 0; n < QB; ++n)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) settle(st.qf[n][s]);
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
@@ -488,6 +492,8 @@ __global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
   };
   kdma.issue(buf0, Kg, 0, len, stride, w, lane);
   vdma.issue(buf0 + L::KSZ, Vg, 0, len, stride, w, lane);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) settle(st.qf[0][s]);
   wait_vmem();
   for (int kt = 0; kt < n_kt; kt += 2) {
     // One wave: its LDS reads of a buffer are consumed by its MFMAs before the next

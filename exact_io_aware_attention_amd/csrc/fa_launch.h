@@ -20,6 +20,7 @@ struct Problem {
   void* dk;
   void* dv;
   float* dvec;         // backward workspace: D_i = rowsum(dO * O), same layout as lse
+  float* mneg;         // backward workspace: -LSE_i / scale, same layout as lse
   const int32_t* cu_seqlens;  // NULL: padded batch
   int batch, heads, seqlen, head_dim;
   int total_tokens;    // batch * seqlen, or the packed token count
@@ -31,7 +32,7 @@ struct Problem {
 // Each launcher enqueues one kernel on p.stream and returns hipGetLastError().
 hipError_t launch_fwd_bf16(const Problem& p);
 hipError_t launch_fwd_fp32(const Problem& p);
-hipError_t launch_bwd_pre(const Problem& p, bool fp32);   // D = rowsum(dO * O)
+hipError_t launch_bwd_pre(const Problem& p, bool fp32);   // D = rowsum(dO * O), -LSE / scale
 hipError_t launch_bwd_dkdv_bf16(const Problem& p);
 hipError_t launch_bwd_dq_bf16(const Problem& p);
 hipError_t launch_bwd_dkdv_fp32(const Problem& p);

@@ -79,10 +79,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the fp32 row statistic
- * D_i = sum_k dO_ik * O_ik, one per (head, query row), rounded up to 256 bytes.
- * For a packed batch (varlen != 0) pass total_tokens; otherwise it is ignored.
- * Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs: two fp32 row statistics per (head, query
+ * row), D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale, each array rounded up to
+ * 256 bytes. For a packed batch (varlen != 0) pass total_tokens; otherwise it is
+ * ignored. Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
                               int varlen, int total_tokens);
@@ -92,12 +92,14 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
  * by fa_fwd and the caller) and lse (from fa_fwd); writes dq, dk, dv in the dtype and
  * layout of q. P is recomputed tile by tile from lse, never stored ("Recalcular en vez
  * de guardar"). Three kernels run on `stream` (the stages below, in order):
- *   1. D_i = rowsum(dO * O) for every query row, into the workspace;
+ *   1. D_i = rowsum(dO * O) and -LSE_i / softmax_scale for every query row, into the
+ *      workspace;
  *   2. one workgroup per (sequence, head, key tile) accumulating dK and dV on chip
  *      while it walks the query tiles;
  *   3. the dQ accumulation pass: one workgroup per (sequence, head, query tile)
  *      accumulating dQ on chip while it walks the key tiles.
  * No atomics: the result is bitwise deterministic from run to run.
+ * softmax_scale must be finite and nonzero (the backward works with LSE / scale).
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller; its contents on entry do not matter.
  */
@@ -116,16 +118,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * fa_bwd_dq start; those two only read the workspace and may run concurrently on
  * different streams. Each enqueues exactly one kernel.
  *
- *  fa_bwd_preprocess: workspace <- D_i = sum_k dO_ik * O_ik (fp32, lse layout). D is
- *    the row sum of P * dP, the term the softmax backward subtracts; computing it from
- *    the stored O avoids touching P ("Recalcular en vez de guardar").
+ *  fa_bwd_preprocess: workspace <- D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale
+ *    (fp32, lse layout each). D is the row sum of P * dP, the term the softmax backward
+ *    subtracts; computing it from the stored O avoids touching P ("Recalcular en vez
+ *    de guardar"). The second array is the starting value of the S = Q K^T
+ *    accumulation in fa_bwd_dkdv, so that P = exp2(scale * log2(e) * (S - LSE / scale))
+ *    needs no per-row term afterwards.
  *  fa_bwd_dkdv: dk, dv. One workgroup per (sequence, head, key tile) accumulates dK and
  *    dV on chip while walking the query tiles, recomputing P from lse.
  *  fa_bwd_dq: dq. One workgroup per (sequence, head, query tile) accumulates dQ on chip
  *    while walking the key tiles, recomputing P from lse.
  */
-int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
-                      int batch, int heads, int seqlen, int head_dim,
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int batch, int heads, int seqlen, int head_dim, float softmax_scale,
                       const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,

@@ -97,6 +97,7 @@ def test_fwd_argument_checks(kw, code):
     (dict(dv=MIS), fa.FA_ERR_INVALID_ARG),
     (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
     (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),   # the backward works with LSE / scale
     (dict(workspace_bytes=255), fa.FA_ERR_WORKSPACE),
     (dict(workspace=A + 16), fa.FA_ERR_WORKSPACE),
     (dict(seqlen=-5), fa.FA_ERR_INVALID_ARG),
@@ -112,9 +113,14 @@ def test_stage_argument_checks():
     common = dict(batch=1, heads=2, seqlen=16, head_dim=64, cu_seqlens=None, total_tokens=0,
                   dtype=fa.FA_DTYPE_BF16, stream=None)
     ws = dict(workspace=A, workspace_bytes=1 << 20)
-    assert fa.fa_bwd_preprocess(o=None, dout=A, **ws, **common) == fa.FA_ERR_INVALID_ARG
-    assert fa.fa_bwd_preprocess(o=A, dout=A, workspace=None, workspace_bytes=0, **common) == fa.FA_ERR_WORKSPACE
-    assert fa.fa_bwd_preprocess(o=A, dout=A, **ws, **dict(common, head_dim=48)) == fa.FA_ERR_UNSUPPORTED
+    pre = dict(softmax_scale=0.125)
+    assert fa.fa_bwd_preprocess(o=None, dout=A, lse=A, **ws, **pre, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=None, **ws, **pre, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=MIS, **ws, **pre, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, workspace=None, workspace_bytes=0, **pre,
+                                **common) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, **ws, softmax_scale=0.0, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, **ws, **pre, **dict(common, head_dim=48)) == fa.FA_ERR_UNSUPPORTED
     sc = dict(softmax_scale=0.125, causal=1)
     assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=None, dv=A, **ws, **sc, **common) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=A, dv=A, workspace=A, workspace_bytes=64,
@@ -126,9 +132,10 @@ def test_stage_argument_checks():
 
 def test_workspace_size():
     _lib()
-    assert fa.fa_bwd_workspace_bytes(4, 32, 4096, 128, 0, 0) == 4 * 32 * 4096 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 3, 5, 64, 0, 0) == 256
-    assert fa.fa_bwd_workspace_bytes(7, 32, 2048, 128, 1, 16384) == 32 * 16384 * 4
+    # two fp32 arrays (D and -LSE / scale), each rounded up to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(4, 32, 4096, 128, 0, 0) == 2 * 4 * 32 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 3, 5, 64, 0, 0) == 2 * 256
+    assert fa.fa_bwd_workspace_bytes(7, 32, 2048, 128, 1, 16384) == 2 * 32 * 16384 * 4
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 80, 0, 0) == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64, 0, 0) == 0
 
