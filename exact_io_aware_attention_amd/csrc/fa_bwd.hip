@@ -119,7 +119,7 @@ constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;  // keys per workgroup
 constexpr int kKvBQ = 64;             // queries per tile: two 32-query blocks
-constexpr int kKvPf = 3;              // operand reads run this many MFMA steps ahead
+constexpr int kKvPf = 2;              // operand reads run this many MFMA steps ahead
 // LDS buffers of the head_dim-128 kernel: four (two tiles in flight while one is read;
 // they fill the 160 KB).
 constexpr int kKvStages = 4;
@@ -170,6 +170,13 @@ __device__ __forceinline__ void kv_init_s(KvBlock& b, const u16* buf, int r0, in
   for (int e = 0; e < 4; ++e) b.s[4 * r4 + e] = m4[e];
 }
 
+template <int D>
+__device__ __forceinline__ void kv_init_dp(KvBlock& b, const u16* buf, int r0, int r4, int g) {
+  const f32x4 d4 = kv_stat4<D>(buf, 1, r0, r4, g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b.dp[4 * r4 + e] = d4[e];
+}
+
 // dV^T / dK^T accumulation step. At head_dim 128 the accumulators (128 registers) are
 // pinned in AGPRs, leaving the VGPRs to the score arithmetic; at 64 they fit anyway.
 template <int D>
@@ -186,22 +193,24 @@ __device__ __forceinline__ void kv_acc_fence(f32x16& acc) {
   if constexpr (D == 128) agpr_acc_fence(acc);
 }
 
-// Row-wise operand j of the S / dP products of the block at rows r0 of tile buffer
-// `buf`: Q rows (slices 0 .. NS-1) for S, then dO rows for dP.
+// Row-wise operand of step j of the S / dP products of the block at rows r0 of tile
+// buffer `buf`: the two products alternate (even steps: Q slice j / 2 for S, odd
+// steps: dO slice j / 2 for dP), so that no MFMA waits for the one just before it.
 template <int D>
 __device__ __forceinline__ bf16x8 kv_row_operand(const u16* buf, int r0, int j, int lane) {
-  constexpr int NS = D / 16;
-  return j < NS ? swz_row_operand<D>(buf, r0, j, lane)
-                : swz_row_operand<D>(buf + KvLds<D>::TSZ, r0, j - NS, lane);
+  return swz_row_operand<D>((j & 1) ? buf + KvLds<D>::TSZ : buf, r0, j >> 1, lane);
 }
 
-// Transposed operand j of the dV / dK products of the block at rows r0: dO^T slices
-// (for dV^T += dO^T P), then Q^T slices (for dK^T += Q^T dS), k-slots in C-row order.
+// Transposed operand of step j of the dV / dK products of the block at rows r0: dO^T
+// (for dV^T += dO^T P) in steps 0 .. NT-1, then Q^T (for dK^T += Q^T dS). Within a
+// product, step jj covers head-dim columns 32 (jj % NB) .. (accumulator jj % NB) and
+// query rows 16 (jj / NB) .. (k-slots in C-row order), so consecutive MFMAs update
+// different accumulators.
 template <int D>
 __device__ __forceinline__ bf16x8 kv_tr_operand(const u16* buf, int r0, int j, int lane) {
-  constexpr int NT = D / 16;  // operands per product
-  const int i = j % NT;
-  return swz_tr_operand<D>(j < NT ? buf + KvLds<D>::TSZ : buf, r0 + 16 * (i & 1), 32 * (i >> 1), lane);
+  constexpr int NT = D / 16, NB = D / 32;  // operands per product, accumulators
+  const int jj = j % NT;
+  return swz_tr_operand<D>(j < NT ? buf + KvLds<D>::TSZ : buf, r0 + 16 * (jj / NB), 32 * (jj % NB), lane);
 }
 
 // Softmax step for element r of block b (query qc + crow_nat(r, g)): P = exp2(c (S -
@@ -223,14 +232,16 @@ __device__ __forceinline__ void kv_softmax_one(KvBlock& b, bf16x8 (&pb)[2], bf16
   if (r % 8 == 7) {
     pb[r / 8] = to_bf16x8(half_of(b.s, r / 8));
     db[r / 8] = to_bf16x8(half_of(b.dp, r / 8));
+    // keep the conversions in this step too (they would sink to phase Y's first MFMA)
+    asm volatile("" : "+v"(pb[r / 8]), "+v"(db[r / 8]));
   }
 }
 
 // Phase X. The matrix pipe computes S and D - dP of block nx (rows rn of tile buffer
 // bn; when NXT) while the vector ALUs run the softmax step of block cu (query rows
 // qc.., tile buffer bc, rows rc; when CUR). rop holds the first kKvPf row operands of
-// nx and nx.s its starting value, read beforehand; D is read here into nx.dp; the last
-// steps read the first kKvPf transposed operands of phase Y for cu into top.
+// nx, and nx.s and nx.dp their starting values, read beforehand; the last steps read
+// the first kKvPf transposed operands of phase Y for cu into top.
 template <int D, bool CAUSAL, bool NXT, bool CUR, bool MASK>
 __device__ __forceinline__ void kv_phase_x(const KvState<D>& st, KvBlock& nx, const u16* bn, int rn,
                                            bf16x8 (&rop)[kKvPf], KvBlock& cu, bf16x8 (&pb)[2], bf16x8 (&db)[2],
@@ -238,23 +249,15 @@ __device__ __forceinline__ void kv_phase_x(const KvState<D>& st, KvBlock& nx, co
                                            float c, int lane) {
   constexpr int NS = D / 16, NX = 2 * NS, EPS = 16 / NX;
   const int g = lane >> 5;
-  if constexpr (NXT) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 d4 = kv_stat4<D>(bn, 1, rn, r4, g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) nx.dp[4 * r4 + e] = d4[e];
-    }
-  }
 #pragma unroll
   for (int j = 0; j < NX; ++j) {
     if constexpr (NXT) {
       const bf16x8 a = rop[j % kKvPf];
       if (j + kKvPf < NX) rop[j % kKvPf] = kv_row_operand<D>(bn, rn, j + kKvPf, lane);
-      if (j < NS)
-        nx.s = mfma32(a, st.kf[j], nx.s);
+      if ((j & 1) == 0)
+        nx.s = mfma32(a, st.kf[j >> 1], nx.s);
       else
-        nx.dp = mfma32(a, st.vf[j - NS], nx.dp);
+        nx.dp = mfma32(a, st.vf[j >> 1], nx.dp);
     }
     if constexpr (CUR) {
 #pragma unroll
@@ -268,25 +271,26 @@ __device__ __forceinline__ void kv_phase_x(const KvState<D>& st, KvBlock& nx, co
 // Phase Y for block cu (rows rc of tile buffer bc): dV^T += dO^T P, then
 // -dK^T += Q^T (-dS), with the transposed operands read kKvPf steps ahead (the first
 // ones in phase X). When NXT, the last steps read the first row operands and the
-// starting value of S of the block the next phase X computes (nx: rows rn of tile
-// buffer bn).
+// starting values of S and dP of the block the next phase X computes (nx: rows rn of
+// tile buffer bn).
 template <int D, bool NXT>
 __device__ __forceinline__ void kv_phase_y(KvState<D>& st, const u16* bc, int rc, const bf16x8 (&pb)[2],
                                            const bf16x8 (&db)[2], bf16x8 (&top)[kKvPf], const u16* bn, int rn,
                                            bf16x8 (&rop)[kKvPf], KvBlock& nx, int lane) {
-  constexpr int NT = D / 16, NY = 2 * NT;
-  static_assert(NY >= 4 && NY >= kKvPf, "the prefetches need four steps");
+  constexpr int NT = D / 16, NB = D / 32, NY = 2 * NT;
+  static_assert(NY >= 8 && NY >= kKvPf, "the prefetches need eight steps");
 #pragma unroll
   for (int j = 0; j < NY; ++j) {
     const bf16x8 a = top[j % kKvPf];
     if (j + kKvPf < NY) top[j % kKvPf] = kv_tr_operand<D>(bc, rc, j + kKvPf, lane);
-    const int i = j % NT;
+    const int jj = j % NT;
     if (j < NT)
-      kv_acc_mfma<D>(st.dvT[i >> 1], a, pb[i & 1]);
+      kv_acc_mfma<D>(st.dvT[jj % NB], a, pb[jj / NB]);
     else
-      kv_acc_mfma<D>(st.dkT[i >> 1], a, db[i & 1]);
+      kv_acc_mfma<D>(st.dkT[jj % NB], a, db[jj / NB]);
     if constexpr (NXT) {
       if (j >= NY - kKvPf) rop[j - (NY - kKvPf)] = kv_row_operand<D>(bn, rn, j - (NY - kKvPf), lane);
+      if (j >= NY - 8 && j < NY - 4) kv_init_dp<D>(nx, bn, rn, j - (NY - 8), lane >> 5);
       if (j >= NY - 4) kv_init_s<D>(nx, bn, rn, j - (NY - 4), lane >> 5);
     }
     step_fence();
@@ -435,13 +439,19 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
 #pragma unroll
     for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 0, j, lane);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) kv_init_s<D>(blk0, bf, 0, r4, g);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      kv_init_s<D>(blk0, bf, 0, r4, g);
+      kv_init_dp<D>(blk0, bf, 0, r4, g);
+    }
     kv_phase_x<D, CAUSAL, true, false, false>(st, blk0, bf, 0, rop, blk1, pb, db, bf, 0, top, 0, kj, len, p.c,
                                               lane);
 #pragma unroll
     for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 32, j, lane);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) kv_init_s<D>(blk1, bf, 32, r4, g);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      kv_init_s<D>(blk1, bf, 32, r4, g);
+      kv_init_dp<D>(blk1, bf, 32, r4, g);
+    }
   };
   // The collective step between the two blocks of tile qt: wait for tile qt + 1 (tiles
   // up to qt + S - 2 may still be in flight), barrier, then refill the buffer of tile
