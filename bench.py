@@ -42,21 +42,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 754627515, "fetch_kib": 301904.9, "write_kib": 133142.8,
+    ("c3", "fwd"): {"bytes": 747096546, "fetch_kib": 298239.9, "write_kib": 133120.1,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
+                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 276877332, "fetch_kib": 131100.5, "write_kib": 8192.0,
+    ("c3", "bwd_preprocess"): {"bytes": 293649624, "fetch_kib": 135194.6, "write_kib": 16384.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
+                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 944048583, "fetch_kib": 328565.6, "write_kib": 264804.0,
+    ("c3", "bwd_dkdv"): {"bytes": 913429367, "fetch_kib": 312483.3, "write_kib": 267068.2,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
+                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 909685460, "fetch_kib": 376525.2, "write_kib": 135328.8,
+    ("c3", "bwd_dq"): {"bytes": 888123859, "fetch_kib": 368083.0, "write_kib": 131159.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "33436c25d178a68eb14d7a9ddbeac3274873d047562d9750ce8407bbfe435144",
+                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
