@@ -801,13 +801,12 @@ constexpr int kDqBR = 32 * kDqWaves;  // queries per workgroup
 constexpr int kDqBC = 64;             // keys per tile
 
 // One double-buffered half: K (read row-wise for S^T and transposed for dQ) and V
-// (row-wise for dP^T).
+// (row-wise for dP^T), both swizzled tiles (conflict-free both ways; one layout for both
+// lets a single set of copy offsets serve K and V; the pads are unused).
 template <int D>
 struct DqLds {
-  // V is read row-wise only, but pitch_both is conflict-free for row reads too, and one
-  // pitch for both tiles lets a single set of copy offsets serve K and V.
-  static constexpr int KP = pitch_both<D>();
-  static constexpr int VP = pitch_both<D>();
+  static constexpr int KP = swz_pitch<D>();
+  static constexpr int VP = swz_pitch<D>();
   static constexpr int KSZ = kDqBC * KP;
   static constexpr int BUF = KSZ + kDqBC * VP;
 };
@@ -827,29 +826,26 @@ struct DqState {
 //   g holds key k0 + 32j + crow_nat(r, g) against query qi;
 //   P = exp2(c S - LSE log2e), dS = P (dP - D);
 //   dQ^T += K^T dS^T, whose A rows (head-dim entries) are read transposed from the
-//   row-major K tile with k-slots keys 16t + 4g + {0..3, 8..11}.
+//   (swizzled) K tile with k-slots keys 16t + 4g + {0..3, 8..11}.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, int len, int qi, int lane,
                                         float c, bool mask) {
   constexpr int NB = D / 32, NS = D / 16, NJ = kDqBC / 32;
-  constexpr int KP = DqLds<D>::KP, VP = DqLds<D>::VP;
   const u16* Ks = buf;
   const u16* Vs = buf + DqLds<D>::KSZ;
-  const int lr = lane & 31, g = lane >> 5;
+  const int g = lane >> 5;
 
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
     {
-      const u16* kr = Ks + (32 * j + lr) * KP + 8 * g;
-      const u16* vr = Vs + (32 * j + lr) * VP + 8 * g;
-      bf16x8 ak = ld16(kr), av = ld16(vr);
+      bf16x8 ak = swz_row_operand<D>(Ks, 32 * j, 0, lane), av = swz_row_operand<D>(Vs, 32 * j, 0, lane);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         bf16x8 nk = ak, nv = av;
         if (s + 1 < NS) {
-          nk = ld16(kr + 16 * (s + 1));
-          nv = ld16(vr + 16 * (s + 1));
+          nk = swz_row_operand<D>(Ks, 32 * j, s + 1, lane);
+          nv = swz_row_operand<D>(Vs, 32 * j, s + 1, lane);
         }
         sacc = mfma32(ak, st.qf[s], sacc);
         dpacc = mfma32(av, st.dof[s], dpacc);
@@ -869,12 +865,12 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - st.dd);
     const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
-    bf16x8 a = lds_tr_operand(Ks, KP, 32 * j, 0, lane);
+    bf16x8 a = swz_tr_operand<D>(Ks, 32 * j, 0, lane);
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
       const int bb = i >> 1, h = i & 1;
       bf16x8 na = a;
-      if (i + 1 < 2 * NB) na = lds_tr_operand(Ks, KP, 32 * j + 16 * ((i + 1) & 1), 32 * ((i + 1) >> 1), lane);
+      if (i + 1 < 2 * NB) na = swz_tr_operand<D>(Ks, 32 * j + 16 * ((i + 1) & 1), 32 * ((i + 1) >> 1), lane);
       st.dqT[bb] = mfma32(a, h ? ds1 : ds0, st.dqT[bb]);
       a = na;
     }
@@ -920,7 +916,7 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
   const int n_kt = (kv_end + BC - 1) / BC;
 
   static_assert(L::KP == L::VP, "K and V tiles share their copy offsets");
-  TileDma<BC, D, L::KP, kDqWaves> kvdma;
+  TileDma<BC, D, L::KP, kDqWaves, true, false> kvdma;
   kvdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
     kvdma.issue(buf, Kg, kt * BC, len, stride, w, lane);

@@ -266,9 +266,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // With SWZ the tile is a swizzled one (PITCH == swz_pitch<D>()): each lane fetches the
-// chunk whose swizzled position is the slot it writes, and lanes on a pad chunk copy
-// nothing (the pads stay free).
-template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false>
+// chunk whose swizzled position is the slot it writes. Lanes on a pad chunk copy nothing
+// when FREE_PADS (the pads then hold other data), else the row's first chunk (no mask).
+template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false, bool FREE_PADS = SWZ>
 struct TileDma {
   static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
   static_assert(!SWZ || (PITCH == D + 32 && ROWS % 16 == 0), "swizzled tiles: pitch D + 32, 16-row aligned");
@@ -303,7 +303,7 @@ struct TileDma {
       const int L = 64 * copy_index(w, i) + lane;
       const int row = L / CPP, c = L % CPP;
       off[i] = (uint32_t)(((size_t)row * stride + 8 * src_chunk(row, c)) * sizeof(u16));
-      if (SWZ && c >= D / 8) pad_bits |= 1u << i;
+      if (SWZ && FREE_PADS && c >= D / 8) pad_bits |= 1u << i;
     }
   }
 
@@ -318,7 +318,7 @@ struct TileDma {
       const char* base = reinterpret_cast<const char*>(src + (size_t)r0 * stride);
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i)
-        if (!SWZ || !((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * copy_index(w, i));
+        if (!(SWZ && FREE_PADS) || !((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * copy_index(w, i));
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -327,7 +327,7 @@ struct TileDma {
         const int row = L / CPP, c = L % CPP;
         const int grow = min(r0 + row, len - 1);
         const u16* g = src + (size_t)grow * stride + 8 * src_chunk(row, c);
-        if (!SWZ || c < D / 8) dma_lds_b128(g, dst + 512 * k);
+        if (!(SWZ && FREE_PADS) || c < D / 8) dma_lds_b128(g, dst + 512 * k);
       }
     }
 #endif
