@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s, bf16 d=128 N=4096 causal; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA, published (twice bf16)
 CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 
 # HBM traffic per launch of a kernel, from two rocprofv3 --pmc passes over this script
@@ -188,6 +189,47 @@ def decode_bench(reps: int = 20):
     return res
 
 
+def fp8_bench(reps: int = 20):
+    """fa_fwd_fp8 on the 8-bit workloads: median time of `reps` calls (HIP events on the
+    launch stream) and the forward's algorithmic FLOPs (2 GEMM units, halved under causal)
+    per second against the fp8 MFMA peak."""
+    import torch
+    import exact_io_aware_attention_amd as fa
+    import workloads as W
+    res = {}
+    for name, w in sorted(W.FP8_WORKLOADS.items()):
+        q8, k8, v8 = (t.cuda() for t in W.make_fp8_inputs(w))
+        B, N, H, d = q8.shape
+        o = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16)
+        lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+        sp = torch.cuda.current_stream().cuda_stream
+
+        def call():
+            st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                               w.scale, w.descale_q, w.descale_k, w.descale_v, int(w.causal), sp)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_fwd_fp8")
+
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        flops = 2 * (2.0 * B * H * N * N * d) * (0.5 if w.causal else 1.0)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"workload": w.description, "batch": B, "heads": H, "seqlen": N, "head_dim": d,
+                     "causal": w.causal, "ms": round(ms, 4), "tflops": round(tf, 2), "bound": "mfma",
+                     "peak_tflops": PEAK_FP8_TFLOPS, "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del q8, k8, v8, o, lse
+    return res
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """Time the oracle (fp64, NumPy) on whole heads of the workload until ~budget_s."""
     import numpy as np
@@ -234,6 +276,7 @@ def main(argv=None) -> int:
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (not varlen)")
     ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (not varlen)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit forward measurement")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-attention comparison (materialised N x N scores)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -401,6 +444,9 @@ def main(argv=None) -> int:
     if not a.no_decode:
         log("bench: decode workloads")
         out["decode"] = decode_bench()
+    if not a.no_fp8:
+        log("bench: 8-bit forward")
+        out["fp8_forward"] = fp8_bench()
     if a.cpu_budget > 0 and w.varlen is False:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)

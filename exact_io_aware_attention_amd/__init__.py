@@ -4,9 +4,9 @@ A thin Python binding over ``libfa.so``, whose C ABI is declared in ``include/fa
 The raw entry points keep the C names and take integer device pointers:
 
     fa_fwd, fa_bwd, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_workspace_bytes,
-    fa_strerror
+    fa_fwd_decode, fa_fwd_decode_workspace_bytes, fa_fwd_fp8, fa_strerror
 
-``forward`` and ``backward`` marshal torch tensors (device memory and the current
+``forward``, ``backward``, ``decode`` and ``forward_fp8`` marshal torch tensors (device memory and the current
 stream) into those calls; every step of the computation runs in the HIP kernels.
 There is no fallback: if ``libfa.so`` is missing or fails to load, every call raises.
 Build it with ``python -m exact_io_aware_attention_amd.build``.
@@ -22,7 +22,8 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
-    "fa_strerror", "forward", "backward",
+    "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
+    "fa_fwd_fp8", "forward_fp8",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
@@ -66,6 +67,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, f32, f32, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
     lib.fa_fwd_decode.restype = i32
     lib.fa_fwd_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_fwd_decode_workspace_bytes.restype = sz
@@ -120,6 +123,13 @@ def fa_bwd_dq(q: int, k: int, v: int, dout: int, lse: int, workspace: int, works
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen: int, head_dim: int, varlen: int,
                            total_tokens: int) -> int:
     return load_library().fa_bwd_workspace_bytes(batch, heads, seqlen, head_dim, int(varlen), total_tokens)
+
+
+def fa_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, batch: int, heads: int, seqlen: int, head_dim: int,
+               softmax_scale: float, descale_q: float, descale_k: float, descale_v: float, causal: int,
+               stream: Optional[int]) -> int:
+    return load_library().fa_fwd_fp8(q, k, v, o, lse, batch, heads, seqlen, head_dim, softmax_scale, descale_q,
+                                     descale_k, descale_v, int(causal), stream)
 
 
 def fa_fwd_decode(q: int, k: int, v: int, o: int, lse: int, batch: int, heads: int, seqlen_q: int,
@@ -243,3 +253,29 @@ def decode(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
     if st != FA_OK:
         raise FAError(st, "fa_fwd_decode")
     return out, lse
+
+
+def forward_fp8(q8, k8, v8, descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
+                causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse=None,
+                stream=None) -> Tuple:
+    """O (bf16) and LSE of attention on E4M3 inputs (see fa_fwd_fp8 in include/fa.h).
+    q8, k8, v8: (batch, seqlen, heads, head_dim) uint8 tensors of E4M3 codes on the GPU;
+    the real inputs are descale * code value."""
+    import torch
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous 4-d uint8 CUDA tensors")
+    if q8.shape != k8.shape or q8.shape != v8.shape:
+        raise ValueError("q8, k8 and v8 must have the same shape")
+    B, N, H, d = q8.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+    st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                    scale, float(descale_q), float(descale_k), float(descale_v), int(causal), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
+    return out, lse
+

@@ -122,6 +122,35 @@ FA_EXPORT int fa_fwd(const void* q, const void* k, const void* v, void* o, float
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+FA_EXPORT int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
+                         int seqlen, int head_dim, float softmax_scale, float descale_q, float descale_k,
+                         float descale_v, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse)) return FA_ERR_INVALID_ARG;
+  if (!isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v)) return FA_ERR_INVALID_ARG;
+  fa::Problem chk{};
+  const int st = check_common(batch, heads, seqlen, head_dim, softmax_scale, causal, nullptr, 0, FA_DTYPE_BF16,
+                              chk);
+  if (st != FA_OK) return st;
+  fa::Fp8Problem pr{};
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.o = o;
+  pr.lse = lse;
+  pr.batch = batch;
+  pr.heads = heads;
+  pr.seqlen = seqlen;
+  pr.head_dim = head_dim;
+  pr.scale = softmax_scale;
+  pr.descale_q = descale_q;
+  pr.descale_k = descale_k;
+  pr.descale_v = descale_v;
+  pr.causal = causal != 0;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(fa::launch_fwd_fp8(pr));
+}
+
 FA_EXPORT size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim, int varlen, int total_tokens) {
   if (batch < 1 || heads < 1 || seqlen < 1) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;

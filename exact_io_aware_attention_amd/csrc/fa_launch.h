@@ -42,6 +42,21 @@ hipError_t launch_bwd_dq_fp32(const Problem& p);
 // into num_splits splits of split_len keys (a multiple of 64) whose partial results
 // (O normalised by its own sum, fp32, and the split's logsumexp) go to the workspace and
 // are merged by logsumexp weights.
+// Forward pass on OCP FP8 E4M3 inputs with per-tensor descale factors (bf16 O).
+struct Fp8Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int batch, heads, seqlen, head_dim;
+  float scale, descale_q, descale_k, descale_v;
+  bool causal;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_fp8(const Fp8Problem& p);
+
 struct DecodeProblem {
   const void* q;
   const void* k;

@@ -173,6 +173,25 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
                   float softmax_scale, int causal, int num_splits,
                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * Forward pass on 8-bit inputs ([SA] "FlashAttention-2 (PT)", "Comparação com versões
+ * subsequentes": the later FlashAttention-3 adds 8-bit floating point). q, k, v are
+ * (batch, seqlen, heads, head_dim) arrays of OCP FP8 E4M3 codes (one byte each: sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN) and
+ * the real inputs are descale_q * q, descale_k * k, descale_v * v. Writes o (bf16, same
+ * layout, head_dim 64 or 128) and lse (fp32, (batch, heads, seqlen), natural log of the
+ * scaled scores' row sums, as fa_fwd). causal: query i sees key j iff j <= i.
+ * Both products run on 8-bit MFMAs: the scores S = Q K^T accumulate in fp32, and the
+ * probabilities are rounded to E4M3 (round to nearest even, relative error <= 2^-4)
+ * before P V; the row sums use the unrounded fp32 P. O therefore differs from the exact
+ * attention of the real inputs by about 2^-4 / sqrt(3) of its size in relative L2 (the
+ * tests allow 5e-2). Padded batches only (no cu_seqlens). All pointers 16-byte aligned.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int batch, int heads, int seqlen, int head_dim,
+               float softmax_scale, float descale_q, float descale_k, float descale_v,
+               int causal, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -20,3 +20,4 @@ from .attention import (  # noqa: F401
     head_decode,
     decode,
 )
+from .fp8 import e4m3_decode, forward_fp8  # noqa: F401

@@ -26,13 +26,13 @@ def _lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess",
                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
-                                    "fa_fwd_decode_workspace_bytes", "fa_strerror"]
+                                    "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -203,3 +203,31 @@ def test_decode_workspace_size():
     assert fa.fa_fwd_decode_workspace_bytes(2, 3, 5, 200, 64, 3) == (want + 255) // 256 * 256
     assert fa.fa_fwd_decode_workspace_bytes(1, 1, 33, 100, 128, 0) == 0   # unsupported
     assert fa.fa_fwd_decode_workspace_bytes(1, 1, 1, 100, 128, 3) == 0    # > ceil(100 / 64) splits
+
+
+# ---------------------------------------------------------------- 8-bit forward
+
+def _fp8(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, batch=1, heads=2, seqlen=100, head_dim=128, softmax_scale=0.1,
+                descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=1, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(o=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen=0), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_q=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_v=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fp8_argument_checks(kw, code):
+    _lib()
+    assert _fp8(**kw) == code
+

@@ -218,3 +218,52 @@ def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None, *, batch: 
     k = _randn((B, Nk, H, d), seed + 1, w.std, torch.bfloat16)
     v = _randn((B, Nk, H, d), seed + 2, w.std, torch.bfloat16)
     return q, k, v
+
+
+# ---------------------------------------------------------------- 8-bit inputs
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """Forward pass on OCP FP8 E4M3 inputs with per-tensor descale factors."""
+    name: str
+    batch: int
+    heads: int
+    seqlen: int
+    head_dim: int
+    causal: bool
+    std: float
+    seed: int
+    descale_q: float = 1.0
+    descale_k: float = 1.0
+    descale_v: float = 1.0
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# The Llama-shaped training workload with its inputs stored in 8 bits (the pages name
+# 8-bit floating point for FlashAttention-3 without a workload).
+FP8_WORKLOADS = {
+    "f1": Fp8Workload("f1", 4, 32, 4096, 128, True, 1.0, 3001,
+                      description="c3 shape, E4M3 Q, K, V"),
+}
+
+
+def make_fp8_inputs(w: Fp8Workload, seed: Optional[int] = None, *, batch: Optional[int] = None,
+                    seqlen: Optional[int] = None, heads: Optional[int] = None, head_dim: Optional[int] = None):
+    """Seeded uint8 E4M3 codes q8, k8, v8 (B, N, H, d) on the CPU: iid normal values of
+    standard deviation w.std, each divided by its tensor's descale, rounded to E4M3 by
+    torch's float8_e4m3fn conversion (tensor i from a generator seeded seed + i)."""
+    seed = w.seed if seed is None else seed
+    B = w.batch if batch is None else batch
+    N = w.seqlen if seqlen is None else seqlen
+    H = w.heads if heads is None else heads
+    d = w.head_dim if head_dim is None else head_dim
+    out = []
+    for i, ds in enumerate((w.descale_q, w.descale_k, w.descale_v)):
+        g = torch.Generator().manual_seed(seed + i)
+        x = torch.randn((B, N, H, d), generator=g, dtype=torch.float32) * (w.std / ds)
+        out.append(x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+    return tuple(out)
