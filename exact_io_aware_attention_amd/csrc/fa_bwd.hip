@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   constexpr int BK = kKvBK, BQ = kKvBQ, NS = D / 16, NB = D / 32;
   constexpr int S = kKvStages;
   using L = KvLds<D>;
-  using Dma = TileDma<BQ, D, L::P, kKvWaves, true>;
+  using Dma = TileDma<BQ, D, L::P, kKvWaves, true, 8>;  // statistics in the pads of Q rows 0..7
   __shared__ __attribute__((aligned(16))) u16 lds[S * L::BUF];
 
   const int tid = threadIdx.x;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     u16* buf = bufp(qt);
     const int q0 = qt * BQ;
     tdma.issue(buf, Qg, q0, len, stride, w, lane);
-    tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane);
+    tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane, false);
 #if __HIP_DEVICE_COMPILE__
     // lane 16w + t lands at dst + 4 (16w + t) bytes: dst = pad - 64w bytes puts it at pad + 4t
     const int qq = min(q0 + lane, len - 1);  // rows past the end are masked in the tile
@@ -916,7 +916,7 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
   const int n_kt = (kv_end + BC - 1) / BC;
 
   static_assert(L::KP == L::VP, "K and V tiles share their copy offsets");
-  TileDma<BC, D, L::KP, kDqWaves, true, false> kvdma;
+  TileDma<BC, D, L::KP, kDqWaves, true> kvdma;
   kvdma.init(stride, w, lane);
   auto issue = [&](int kt, u16* buf) {
     kvdma.issue(buf, Kg, kt * BC, len, stride, w, lane);

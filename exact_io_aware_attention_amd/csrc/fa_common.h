@@ -266,9 +266,11 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // With SWZ the tile is a swizzled one (PITCH == swz_pitch<D>()): each lane fetches the
-// chunk whose swizzled position is the slot it writes. Lanes on a pad chunk copy nothing
-// when FREE_PADS (the pads then hold other data), else the row's first chunk (no mask).
-template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false, bool FREE_PADS = SWZ>
+// chunk whose swizzled position is the slot it writes. The pads of rows below
+// FREE_PAD_ROWS hold other data: a copy into such a tile (issue with free_pads) skips
+// those pad chunks (only the copies that reach these rows carry a lane mask); every
+// other pad chunk receives the row's first chunk.
+template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false, int FREE_PAD_ROWS = 0>
 struct TileDma {
   static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
   static_assert(!SWZ || (PITCH == D + 32 && ROWS % 16 == 0), "swizzled tiles: pitch D + 32, 16-row aligned");
@@ -277,6 +279,8 @@ struct TileDma {
   static_assert(TOTAL % 64 == 0, "a tile must be a whole number of 64-chunk copies");
   static constexpr int NINST = TOTAL / 64;
   static constexpr int PER_WAVE = (NINST + NWAVES - 1) / NWAVES;
+  static constexpr int MASK_COPIES = (FREE_PAD_ROWS * CPP + 63) / 64;  // copies that reach those rows
+  static_assert(!FREE_PAD_ROWS || SWZ, "free pads exist in swizzled tiles only");
 
   // Byte offset, from the tile's first row in global memory, of the chunk this lane
   // copies in each of its instructions. It does not depend on the tile, so it is
@@ -284,7 +288,7 @@ struct TileDma {
   // fewer repeats the last one (same bytes to the same place), which keeps the issue
   // free of branches.
   uint32_t off[PER_WAVE];
-  uint32_t pad_bits;  // SWZ: bit i set when this lane's chunk in copy i is a pad chunk
+  uint32_t pad_bits;  // bit i set when this lane's chunk in copy i is a free pad chunk
 
   __device__ __forceinline__ static int copy_index(int w, int i) { return min(w + i * NWAVES, NINST - 1); }
 
@@ -303,7 +307,7 @@ struct TileDma {
       const int L = 64 * copy_index(w, i) + lane;
       const int row = L / CPP, c = L % CPP;
       off[i] = (uint32_t)(((size_t)row * stride + 8 * src_chunk(row, c)) * sizeof(u16));
-      if (SWZ && FREE_PADS && c >= D / 8) pad_bits |= 1u << i;
+      if (c >= D / 8 && row < FREE_PAD_ROWS) pad_bits |= 1u << i;
     }
   }
 
@@ -312,13 +316,20 @@ struct TileDma {
   // compiled for the device only: hipcc's host pass otherwise drops (without a
   // diagnostic) the launch stubs of kernels that inline this control flow.
   __device__ __forceinline__ void issue(u16* dst, const u16* __restrict__ src, int r0, int len, size_t stride,
-                                        int w, int lane) const {
+                                        int w, int lane, bool free_pads = true) const {
 #if __HIP_DEVICE_COMPILE__
     if (r0 + ROWS <= len) {  // wave-uniform: a full tile
       const char* base = reinterpret_cast<const char*>(src + (size_t)r0 * stride);
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i)
-        if (!(SWZ && FREE_PADS) || !((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * copy_index(w, i));
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int k = copy_index(w, i);
+        // i * NWAVES is copy i's smallest index: later copies never reach the free pads
+        if (free_pads && i * NWAVES < MASK_COPIES && k < MASK_COPIES) {  // wave-uniform
+          if (!((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * k);
+        } else {
+          dma_lds_b128(base + off[i], dst + 512 * k);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -327,7 +338,7 @@ struct TileDma {
         const int row = L / CPP, c = L % CPP;
         const int grow = min(r0 + row, len - 1);
         const u16* g = src + (size_t)grow * stride + 8 * src_chunk(row, c);
-        if (!(SWZ && FREE_PADS) || c < D / 8) dma_lds_b128(g, dst + 512 * k);
+        if (!(free_pads && c >= D / 8 && row < FREE_PAD_ROWS)) dma_lds_b128(g, dst + 512 * k);
       }
     }
 #endif
