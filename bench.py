@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 747096546, "fetch_kib": 298239.9, "write_kib": 133120.1,
+    ("c3", "fwd"): {"bytes": 744918572, "fetch_kib": 297173.1, "write_kib": 133124.4,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
+                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 293649624, "fetch_kib": 135194.6, "write_kib": 16384.0,
+    ("c3", "bwd_preprocess"): {"bytes": 293650798, "fetch_kib": 135194.7, "write_kib": 16384.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
+                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 913429367, "fetch_kib": 312483.3, "write_kib": 267068.2,
+    ("c3", "bwd_dkdv"): {"bytes": 909684038, "fetch_kib": 310826.0, "write_kib": 266722.8,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
+                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 888123859, "fetch_kib": 368083.0, "write_kib": 131159.0,
+    ("c3", "bwd_dq"): {"bytes": 881030281, "fetch_kib": 364615.0, "write_kib": 131164.8,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "5fb8a9d7702bcc108274c09fd446554d89490d608eb4aa52f768082fed5f3e08",
+                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
