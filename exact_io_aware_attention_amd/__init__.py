@@ -175,9 +175,34 @@ def _shape(q, cu_seqlens, max_seqlen):
 
 
 def _check(*ts):
+    dev = ts[0].device
     for t in ts:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+        if t.device != dev:
+            raise ValueError(f"all tensors must be on one device ({dev}), got {t.device}")
+
+
+def _expect(name: str, t, shape, dtype) -> None:
+    """The C entry points take bare pointers sized from q's dimensions, so every other
+    tensor is checked here, before any launch, against the shape and dtype it must have."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _lse_shape(B, H, N, T, varlen: bool):
+    return (H, T) if varlen else (B, H, N)
+
+
+def _check_cu(cu_seqlens, B: int) -> None:
+    import torch
+    _expect("cu_seqlens", cu_seqlens, (B + 1,), torch.int32)
+
+
+def _workspace_bytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -190,14 +215,22 @@ def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None
     """O and the fp32 natural-log LSE of exact attention (see include/fa.h)."""
     import torch
     B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
-    _check(q, k, v)
+    varlen = cu_seqlens is not None
+    _expect("k", k, q.shape, q.dtype)
+    _expect("v", v, q.shape, q.dtype)
+    if out is not None:
+        _expect("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _expect("lse", lse, _lse_shape(B, H, N, T, varlen), torch.float32)
+    if varlen:
+        _check_cu(cu_seqlens, B)
+    _check(q, k, v, *(t for t in (out, lse, cu_seqlens) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse_shape = (B, H, N) if cu_seqlens is None else (H, T)
-        lse = torch.empty(lse_shape, device=q.device, dtype=torch.float32)
-    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+        lse = torch.empty(_lse_shape(B, H, N, T, varlen), device=q.device, dtype=torch.float32)
+    cu = cu_seqlens.data_ptr() if varlen else None
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
                 scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
     if st != FA_OK:
@@ -211,17 +244,24 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     """(dQ, dK, dV) for the upstream gradient ``dout`` (see include/fa.h)."""
     import torch
     B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
-    _check(q, k, v, o, lse, dout)
+    varlen = cu_seqlens is not None
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _expect(name, t, q.shape, q.dtype)
+    _expect("lse", lse, _lse_shape(B, H, N, T, varlen), torch.float32)
+    if varlen:
+        _check_cu(cu_seqlens, B)
+    _check(q, k, v, o, lse, dout, *(t for t in (dq, dk, dv, workspace, cu_seqlens) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = fa_bwd_workspace_bytes(B, H, N, d, int(cu_seqlens is not None), T)
+    ws_bytes = fa_bwd_workspace_bytes(B, H, N, d, int(varlen), T)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
-    cu = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    cu = cu_seqlens.data_ptr() if varlen else None
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), _workspace_bytes(workspace),
                 B, H, N, d, scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
@@ -234,11 +274,17 @@ def decode(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
     (see fa_fwd_decode in include/fa.h). q: (batch, seqlen_q, heads, head_dim); k, v:
     (batch, seqlen_k, heads, head_dim); bf16."""
     import torch
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+    if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be (batch, seqlen, heads, head_dim)")
-    _check(q, k, v)
     B, Nq, H, d = q.shape
     Nk = k.shape[1]
+    _expect("k", k, (B, Nk, H, d), q.dtype)
+    _expect("v", v, (B, Nk, H, d), q.dtype)
+    if out is not None:
+        _expect("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _expect("lse", lse, (B, H, Nq), torch.float32)
+    _check(q, k, v, *(t for t in (out, lse, workspace) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -248,7 +294,8 @@ def decode(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
     st = fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
-                       scale, int(causal), num_splits, workspace.data_ptr(), workspace.numel(), _dtype_code(q),
+                       scale, int(causal), num_splits, workspace.data_ptr(), _workspace_bytes(workspace),
+                       _dtype_code(q),
                        _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_decode")
@@ -262,12 +309,16 @@ def forward_fp8(q8, k8, v8, descale_q: float = 1.0, descale_k: float = 1.0, desc
     q8, k8, v8: (batch, seqlen, heads, head_dim) uint8 tensors of E4M3 codes on the GPU;
     the real inputs are descale * code value."""
     import torch
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous 4-d uint8 CUDA tensors")
-    if q8.shape != k8.shape or q8.shape != v8.shape:
-        raise ValueError("q8, k8 and v8 must have the same shape")
+    if q8.dim() != 4:
+        raise ValueError("q8 must be (batch, seqlen, heads, head_dim)")
     B, N, H, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _expect(name, t, q8.shape, torch.uint8)
+    if out is not None:
+        _expect("out", out, q8.shape, torch.bfloat16)
+    if lse is not None:
+        _expect("lse", lse, (B, H, N), torch.float32)
+    _check(q8, k8, v8, *(t for t in (out, lse) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16)
