@@ -82,34 +82,75 @@ __device__ __forceinline__ void load8<float>(const float* p, float* out) {
   }
 }
 
-// One (token, head) row per D/8 lanes: rows are contiguous in memory, so a wave reads
-// a contiguous span of O and dO.
-template <int D, typename T, bool VARLEN>
+// Sum over aligned groups of LANES (8 or 16) lanes, the result in every lane of the group,
+// with DPP lane permutations: swap neighbours, swap pairs, then mirror within 8 and 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 8 || LANES == 16, "groups of 8 or 16 lanes");
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  if constexpr (LANES == 16) x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+
+// D = rowsum(dO * O) and -LSE / scale for 64 consecutive tokens of one (sequence, head)
+// per workgroup (a packed batch is one sequence of total_tokens here: its statistics are
+// laid out (H, total_tokens), those of a padded batch (B, H, N), so in both the 64 values
+// are contiguous). D / 8 lanes reduce one row (8 elements each, a row is contiguous in
+// memory); every load of the workgroup's rows is issued before the first reduction, so
+// each wave keeps all of its rows in flight, and the results leave through LDS as two
+// contiguous 256-byte stores.
+constexpr int kPreTokens = 64;
+
+template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                       const float* __restrict__ lse, float* __restrict__ dvec,
-                                                      float* __restrict__ mneg, float scale, int H, int N,
-                                                      int T_total, long long rows) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+                                                      float* __restrict__ mneg, float scale, int H, int n_seq,
+                                                      int n_tiles) {
+  constexpr int LPR = D / 8;               // lanes per row
+  constexpr int RPP = 256 / LPR;           // rows per pass
+  constexpr int PASSES = kPreTokens / RPP;
+  __shared__ float sd[kPreTokens];
+  // Heads vary fastest: consecutive workgroups read the rows of the same tokens, which
+  // are adjacent in memory (token-major layout), so together they stream it in order.
+  const int h = blockIdx.x % H;
+  const int tile = (blockIdx.x / H) % n_tiles;
+  const int s = blockIdx.x / H / n_tiles;
+  const int sh = s * H + h;                // sequence * H + head
+  const int n0 = tile * kPreTokens;
   const int sub = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    float a[8], bq[8];
-    load8<T>(o + row * D + 8 * sub, a);
-    load8<T>(dout + row * D + 8 * sub, bq);
+  float a[PASSES][8], b[PASSES][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], bq[i], acc);
+  for (int ps = 0; ps < PASSES; ++ps) {
+    // Rows past the end re-read the last row (no branch around the loads, so all of them
+    // are in flight together); their sums are never stored.
+    const int n = min(n0 + ps * RPP + (int)threadIdx.x / LPR, n_seq - 1);
+    const size_t off = (((size_t)s * n_seq + n) * H + h) * D + 8 * sub;
+    load8<T>(o + off, a[ps]);
+    load8<T>(dout + off, b[ps]);
   }
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && sub == 0) {
-    const long long token = row / H;
-    const int h = (int)(row % H);
-    const size_t idx = VARLEN ? (size_t)h * T_total + token
-                              : ((size_t)(token / N) * H + h) * N + (size_t)(token % N);
-    dvec[idx] = acc;
-    mneg[idx] = -lse[idx] / scale;
+  for (int ps = 0; ps < PASSES; ++ps) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(a[ps][i], b[ps][i], acc);
+    acc = group_sum<LPR>(acc);
+    if (sub == 0) sd[ps * RPP + threadIdx.x / LPR] = acc;
+  }
+  __syncthreads();
+  const size_t base = (size_t)sh * n_seq + n0;
+  const int t = threadIdx.x % kPreTokens;
+  if (n0 + t < n_seq) {
+    if (threadIdx.x < kPreTokens)
+      dvec[base + t] = sd[t];
+    else if (threadIdx.x < 2 * kPreTokens)
+      mneg[base + t] = -lse[base + t] / scale;
   }
 }
 
@@ -1027,17 +1068,13 @@ BwdParams make_params(const Problem& pr) {
 
 template <int D, typename T>
 hipError_t launch_pre_t(const Problem& pr) {
-  const long long rows = (long long)pr.total_tokens * pr.heads;
-  constexpr int RPB = 256 / (D / 8);
-  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-  if (pr.cu_seqlens)
-    hipLaunchKernelGGL((bwd_pre_kernel<D, T, true>), grid, dim3(256), 0, pr.stream,
-                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg,
-                       pr.scale, pr.heads, pr.seqlen, pr.total_tokens, rows);
-  else
-    hipLaunchKernelGGL((bwd_pre_kernel<D, T, false>), grid, dim3(256), 0, pr.stream,
-                       static_cast<const T*>(pr.o), static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg,
-                       pr.scale, pr.heads, pr.seqlen, pr.total_tokens, rows);
+  // A packed batch is one sequence of total_tokens tokens.
+  const int n_seqs = pr.cu_seqlens ? 1 : pr.batch;
+  const int n_seq = pr.cu_seqlens ? pr.total_tokens : pr.seqlen;
+  const int n_tiles = (n_seq + kPreTokens - 1) / kPreTokens;
+  const dim3 grid((unsigned)((long long)n_tiles * n_seqs * pr.heads));
+  hipLaunchKernelGGL((bwd_pre_kernel<D, T>), grid, dim3(256), 0, pr.stream, static_cast<const T*>(pr.o),
+                     static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg, pr.scale, pr.heads, n_seq, n_tiles);
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     head_backward,
     forward,
     backward,
+    backward_stats,
     forward_rows,
     backward_query_rows,
     backward_key_rows,

@@ -212,6 +212,17 @@ def backward(q, k, v, do, scale: float, causal: bool,
     return dq, dk, dv
 
 
+def backward_stats(o, do, lse, scale: float, cu_seqlens=None) -> Tuple[Array, Array]:
+    """The two per-row statistics the backward starts from, in the LSE layout ((B, H, N)
+    padded, (H, T) packed): D_i = sum_k dO_ik O_ik of the O given (reading r6: the
+    stored O, not a recomputed one; for the exact O it equals sum_j P_ij dP_ij) and
+    -LSE_i / scale."""
+    o, do, lse = to_f64(o), to_f64(do), to_f64(lse)
+    d_tok = (o * do).sum(axis=-1)                 # (B, N, H) or (T, H)
+    d_row = d_tok.transpose(0, 2, 1) if cu_seqlens is None else d_tok.T
+    return d_row, -lse / scale
+
+
 # ----------------------------------------------------------------------------------------
 # Selected rows of one head (long sequences): the same definition, evaluated only for
 # the rows asked for. q, k, v, do are (N, d) float64; rows/keys are index arrays.

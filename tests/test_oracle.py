@@ -294,3 +294,45 @@ def test_empty_sequence_in_pack():
     q, k, v, do = (_rand(rng, 5, 1, 2) for _ in range(4))
     o, lse = oracle.forward(q, k, v, 1.0, True, cu_seqlens=cu)
     assert o.shape == (5, 1, 2) and np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------- backward statistics
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_stats_equal_the_softmax_identity(causal):
+    """For the exact O, D_i = dO_i . O_i equals sum_j P_ij dP_ij with P from torch's own
+    fp64 softmax and dP = dO V^T: a second route to the same number."""
+    rng = np.random.default_rng(31)
+    B, N, H, d, scale = 2, 9, 3, 5, 0.7
+    q, k, v, do = (_rand(rng, B, N, H, d) for _ in range(4))
+    o, lse = oracle.forward(q, k, v, scale, causal)
+    dvec, mneg = oracle.backward_stats(o, do, lse, scale)
+    assert dvec.shape == (B, H, N) and mneg.shape == (B, H, N)
+    for b, h in itertools.product(range(B), range(H)):
+        s = torch.from_numpy(scale * q[b, :, h] @ k[b, :, h].T)
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        p = torch.softmax(s, dim=-1).numpy()
+        dp = do[b, :, h] @ v[b, :, h].T
+        np.testing.assert_allclose(dvec[b, h], (p * dp).sum(axis=1), atol=1e-12)
+        np.testing.assert_allclose(mneg[b, h], -torch.logsumexp(s, dim=-1).numpy() / scale, atol=1e-12)
+
+
+def test_backward_stats_layouts_by_loops():
+    """Padded (B, H, N) and packed (H, T) layouts against explicit loops, with an O that
+    is not an attention output (reading r6: D comes from whatever O is stored)."""
+    rng = np.random.default_rng(32)
+    B, N, H, d = 2, 4, 3, 2
+    o, do = _rand(rng, B, N, H, d), _rand(rng, B, N, H, d)
+    lse = _rand(rng, B, H, N)
+    dvec, mneg = oracle.backward_stats(o, do, lse, 0.5)
+    for b, n, h in itertools.product(range(B), range(N), range(H)):
+        assert dvec[b, h, n] == pytest.approx(sum(o[b, n, h, j] * do[b, n, h, j] for j in range(d)), abs=1e-14)
+        assert mneg[b, h, n] == pytest.approx(-2.0 * lse[b, h, n], abs=1e-14)
+    T = 7
+    o, do, lse = _rand(rng, T, H, d), _rand(rng, T, H, d), _rand(rng, H, T)
+    dvec, mneg = oracle.backward_stats(o, do, lse, 0.25, cu_seqlens=np.array([0, 3, 7]))
+    assert dvec.shape == (H, T)
+    for t, h in itertools.product(range(T), range(H)):
+        assert dvec[h, t] == pytest.approx(sum(o[t, h, j] * do[t, h, j] for j in range(d)), abs=1e-14)
+        assert mneg[h, t] == pytest.approx(-4.0 * lse[h, t], abs=1e-14)

@@ -45,6 +45,11 @@ MUTATIONS = {
     "decode_mask_off_by_one": ("np.arange(n_k)[None, :] > last_visible[:, None]",
                                "np.arange(n_k)[None, :] >= last_visible[:, None]"),
     "decode_lse_layout": ("o[b, :, h, :], lse[b, h, :] = head_decode", "lse[b, h, :], o[b, :, h, :] = head_decode"),
+    "stats_padded_layout": ("d_tok.transpose(0, 2, 1) if", "d_tok.transpose(0, 1, 2) if"),
+    "stats_packed_layout": ("if cu_seqlens is None else d_tok.T", "if cu_seqlens is None else d_tok"),
+    "stats_mneg_sign": ("return d_row, -lse / scale", "return d_row, lse / scale"),
+    "stats_mneg_times_scale": ("return d_row, -lse / scale", "return d_row, -lse * scale"),
+    "stats_d_from_o_only": ("d_tok = (o * do).sum(axis=-1)", "d_tok = (o * o).sum(axis=-1)"),
 }
 
 
@@ -172,8 +177,27 @@ def _pins(m):
                     s = s.masked_fill(~allowed, float("-inf"))
                 np.testing.assert_allclose(lse[0, h], torch.logsumexp(s, 1).numpy(), atol=1e-12)
 
+    def stats():
+        rng = np.random.default_rng(6)
+        B, N, H, d = 2, 5, 3, 4
+        q, k, v, do = (rng.standard_normal((B, N, H, d)) for _ in range(4))
+        o, lse = m.forward(q, k, v, 0.7, True)
+        dvec, mneg = m.backward_stats(o, do, lse, 0.7)
+        for b, h in itertools.product(range(B), range(H)):
+            s = torch.from_numpy(0.7 * q[b, :, h] @ k[b, :, h].T)
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+            p = torch.softmax(s, dim=-1).numpy()
+            np.testing.assert_allclose(dvec[b, h], (p * (do[b, :, h] @ v[b, :, h].T)).sum(1), atol=1e-12)
+            np.testing.assert_allclose(mneg[b, h], -torch.logsumexp(s, 1).numpy() / 0.7, atol=1e-12)
+        T = 6
+        o, do, lse = rng.standard_normal((T, H, d)), rng.standard_normal((T, H, d)), rng.standard_normal((H, T))
+        dvec, mneg = m.backward_stats(o, do, lse, 0.5, cu_seqlens=np.array([0, 2, 6]))
+        for t, h in itertools.product(range(T), range(H)):
+            np.testing.assert_allclose(dvec[h, t], float(o[t, h] @ do[t, h]), atol=1e-12)
+            np.testing.assert_allclose(mneg[h, t], -2.0 * lse[h, t], atol=1e-12)
+
     for name, fn in (("golden", golden), ("torch", torch_ref), ("fd", finite_differences),
-                     ("rows", row_helpers), ("packed", packed), ("decode", decode)):
+                     ("rows", row_helpers), ("packed", packed), ("decode", decode), ("stats", stats)):
         check(name, fn)
     return failed
 
