@@ -23,7 +23,9 @@
  *    The library never allocates, frees, or synchronises, and keeps no state between
  *    calls. All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and is asynchronous: a device-side fault surfaces on the caller's next
- *    synchronising call, not here.
+ *    synchronising call, not here. The calls enqueue kernel launches only (no memset,
+ *    copy or host synchronisation), so they may be captured in a HIP graph; a
+ *    captured call keeps the pointers and sizes it was captured with.
  *  - Layout: q, k, v, o, dout, dq, dk, dv are contiguous (batch, seqlen, heads,
  *    head_dim), head_dim innermost. With cu_seqlens != NULL (a packed batch) they are
  *    (total_tokens, heads, head_dim) and sequence b owns tokens
