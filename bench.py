@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 744918572, "fetch_kib": 297173.1, "write_kib": 133124.4,
+    ("c3", "fwd"): {"bytes": 746368789, "fetch_kib": 297881.6, "write_kib": 133123.8,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
+                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 293650798, "fetch_kib": 135194.7, "write_kib": 16384.0,
+    ("c3", "bwd_preprocess"): {"bytes": 274770594, "fetch_kib": 132119.8, "write_kib": 4096.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
+                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 909684038, "fetch_kib": 310826.0, "write_kib": 266722.8,
+    ("c3", "bwd_dkdv"): {"bytes": 908041041, "fetch_kib": 310456.8, "write_kib": 265857.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
+                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 881030281, "fetch_kib": 364615.0, "write_kib": 131164.8,
+    ("c3", "bwd_dq"): {"bytes": 879553171, "fetch_kib": 363901.3, "write_kib": 131149.7,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "48ddcf89f0249d2da9d885142bdde0ecc0e646340cfcf622036ad8c9e492b0a7",
+                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
