@@ -284,8 +284,9 @@ def main(argv=None) -> int:
                          "three times, as the known-size reference for HBM byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the attention path has no "
-              "cross-GPU component; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): every (sequence, head) pair is "
+              "independent, so more GPUs would each run these kernels on their share of the heads; no "
+              "cross-GPU path is implemented", file=sys.stderr)
         return 2
 
     import torch
