@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_library_has_no_undefined_internal_symbols():
     """Every kernel launch stub is defined (a host-pass miscompile once left them
-    undefined, which only shows up as a load failure on the GPU machine)."""
+    undefined, which only shows up as a load failure on a machine with a GPU)."""
     _lib()
     out = subprocess.run(["nm", "-D", fa.library_path()], capture_output=True, text=True, check=True).stdout
     missing = [l for l in out.splitlines() if " U " in l and "_ZN2fa" in l]
