@@ -254,21 +254,28 @@ __device__ __forceinline__ bf16x8 kv_tr_operand(const u16* buf, int r0, int j, i
   return swz_tr_operand<D>(j < NT ? buf + KvLds<D>::TSZ : buf, r0 + 16 * (jj / NB), 32 * (jj % NB), lane);
 }
 
-// Softmax step for element r of block b (query qc + crow_nat(r, g)): P = exp2(c (S -
-// LSE / scale)), zero where masked, -dS = P (D - dP); every eighth element, eight of
-// each go to bf16 as half of a B operand.
-template <bool CAUSAL, bool MASK>
-__device__ __forceinline__ void kv_softmax_one(KvBlock& b, bf16x8 (&pb)[2], bf16x8 (&db)[2], int r, int qc, int kj,
-                                               int len, float c, int g) {
+// Softmax of element r of block b (query qc + crow_nat(r, g)) in two parts, one step
+// apart: the exponential P = exp2(c (S - LSE / scale)), then (next step) the mask, -dS =
+// P (D - dP) and, every eighth element, eight of each converted to bf16 as half of a B
+// operand. Done in one step, the multiply would wait on the exponential (a transcendental
+// result needs a wait state before its first use, here an s_nop).
+__device__ __forceinline__ void kv_softmax_exp(KvBlock& b, int r, float c) {
   float e = fast_exp2(b.s[r] * c);
   // Pin the exponential to this step (the compiler would otherwise sink the softmax
   // towards its first use, out of the matrix-pipe phase it is meant to overlap).
   asm volatile("" : "+v"(e));
+  b.s[r] = e;
+}
+
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void kv_softmax_finish(KvBlock& b, bf16x8 (&pb)[2], bf16x8 (&db)[2], int r, int qc,
+                                                  int kj, int len, int g) {
+  float e = b.s[r];
   if constexpr (MASK) {
     const int qq = qc + crow_nat(r, g);
     e = (qq >= len || (CAUSAL && kj > qq)) ? 0.f : e;
+    b.s[r] = e;
   }
-  b.s[r] = e;
   b.dp[r] *= e;
   if (r % 8 == 7) {
     pb[r / 8] = to_bf16x8(half_of(b.s, r / 8));
@@ -302,10 +309,18 @@ __device__ __forceinline__ void kv_phase_x(const KvState<D>& st, KvBlock& nx, co
     }
     if constexpr (CUR) {
 #pragma unroll
-      for (int u = 0; u < EPS; ++u) kv_softmax_one<CAUSAL, MASK>(cu, pb, db, EPS * j + u, qc, kj, len, c, g);
+      for (int u = 0; u < EPS; ++u) kv_softmax_exp(cu, EPS * j + u, c);
+      if (j > 0) {
+#pragma unroll
+        for (int u = 0; u < EPS; ++u) kv_softmax_finish<CAUSAL, MASK>(cu, pb, db, EPS * (j - 1) + u, qc, kj, len, g);
+      }
       if (j >= NX - kKvPf) top[j - (NX - kKvPf)] = kv_tr_operand<D>(bc, rc, j - (NX - kKvPf), lane);
     }
     step_fence();
+  }
+  if constexpr (CUR) {
+#pragma unroll
+    for (int u = 0; u < EPS; ++u) kv_softmax_finish<CAUSAL, MASK>(cu, pb, db, EPS * (NX - 1) + u, qc, kj, len, g);
   }
 }
 
