@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   constexpr int BK = kKvBK, BQ = kKvBQ, NS = D / 16, NB = D / 32;
   constexpr int S = kKvStages;
   using L = KvLds<D>;
-  using Dma = TileDma<BQ, D, L::P, kKvWaves, true, 8>;  // statistics in the pads of Q rows 0..7
+  using Dma = TileDma<BQ, D, L::P, kKvWaves, true, 8, false>;  // statistics in the pads of Q rows 0..7
   __shared__ __attribute__((aligned(16))) u16 lds[S * L::BUF];
 
   const int tid = threadIdx.x;

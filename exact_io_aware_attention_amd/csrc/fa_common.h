@@ -246,6 +246,30 @@ __device__ __forceinline__ void dma_lds_b32(const void* src, const void* dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds_addr(dst)) : "memory");
 }
 
+// The same copy from a wave-uniform base address plus a per-lane 32-bit byte offset: the
+// address add happens in the load, so no 64-bit vector add per copy. The base must be
+// the same in every lane; it is read from the first one (where the compiler cannot
+// prove it uniform it holds it in VGPRs, and v_readfirstlane moves it to SGPRs). The
+// load reads the base from SGPRs that an s_mov in the same asm block has just written:
+// an SGPR written by a vector instruction (such as v_readfirstlane) needs five wait
+// states before a memory instruction may read it, which the compiler cannot see to
+// insert here, while one written by a scalar instruction needs none. The s_mov also
+// provides the wait state after the M0 write.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma_lds_b128(const void* sbase, uint32_t voff, const void* dst) {
+  uint64_t base;
+  asm volatile("s_mov_b64 %0, %2\n\tglobal_load_lds_dwordx4 %1, %0"
+               : "=&s"(base)
+               : "v"(voff), "s"(uniform_ptr(sbase)), "{m0}"(lds_addr(dst))
+               : "memory");
+}
+
 // A use of x that makes the compiler wait here for the loads that produced it. The
 // compiler's own waits are vmcnt(0) (it does not count the asm copies above), so a
 // register loaded before a tile loop and first read inside it would cost a wait inside
@@ -270,7 +294,7 @@ __device__ __forceinline__ void lds_barrier() {
 // FREE_PAD_ROWS hold other data: a copy into such a tile (issue with free_pads) skips
 // those pad chunks (only the copies that reach these rows carry a lane mask); every
 // other pad chunk receives the row's first chunk.
-template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false, int FREE_PAD_ROWS = 0>
+template <int ROWS, int D, int PITCH, int NWAVES, bool SWZ = false, int FREE_PAD_ROWS = 0, bool SADDR = true>
 struct TileDma {
   static_assert(PITCH % 8 == 0, "pitch must be a whole number of 16-byte chunks");
   static_assert(!SWZ || (PITCH == D + 32 && ROWS % 16 == 0), "swizzled tiles: pitch D + 32, 16-row aligned");
@@ -311,6 +335,16 @@ struct TileDma {
     }
   }
 
+  // Copy i of a full tile: from the SGPR base plus this lane's offset, or (SADDR false)
+  // from a 64-bit vector address (measured faster in the dK/dV kernel, whose copies sit
+  // among scalar-heavy code; the others gain from the address add leaving the VALU).
+  __device__ __forceinline__ void copy_full(const char* base, int i, u16* dst) const {
+    if constexpr (SADDR)
+      dma_lds_b128(base, off[i], dst);
+    else
+      dma_lds_b128(base + off[i], dst);
+  }
+
   // Copy rows [r0, r0 + ROWS) of `src` into `dst` (w: the wave index, uniform). Rows at
   // or past `len` are copies of row len - 1 (the consumer masks them). The body is
   // compiled for the device only: hipcc's host pass otherwise drops (without a
@@ -325,9 +359,9 @@ struct TileDma {
         const int k = copy_index(w, i);
         // i * NWAVES is copy i's smallest index: later copies never reach the free pads
         if (free_pads && i * NWAVES < MASK_COPIES && k < MASK_COPIES) {  // wave-uniform
-          if (!((pad_bits >> i) & 1)) dma_lds_b128(base + off[i], dst + 512 * k);
+          if (!((pad_bits >> i) & 1)) copy_full(base, i, dst + 512 * k);
         } else {
-          dma_lds_b128(base + off[i], dst + 512 * k);
+          copy_full(base, i, dst + 512 * k);
         }
       }
     } else {
