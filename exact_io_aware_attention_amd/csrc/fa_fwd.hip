@@ -164,8 +164,35 @@ __device__ __forceinline__ void fwd_scale_o(FwdState<D, QB>& st, const float (&a
     }
 }
 
-// One exponential of block j's scores (value v of QB * 16), its share of the row sum,
-// and, every eighth value, the bf16 conversion of eight of them into P.
+// With two query blocks per wave (one wave per SIMD) each exponential's uses are pinned
+// to the step after it; with one block (two waves per SIMD) they are left to the
+// compiler, which sinks them into the code between phases, where the other wave on
+// the SIMD covers them (measured: pinning costs 1 % at d=128 and gains 4 % at d=64).
+template <int QB>
+constexpr bool fwd_pin_uses() { return QB == 2; }
+
+// The use of exponential v of block j (value v of QB * 16): its share of the row sum
+// (the four partial sums start from values 0..3, not from 0 + x, which does not fold
+// away) and, every eighth value, the bf16 conversion of eight of them into P, pinned to
+// the step it is called in.
+template <int QB>
+__device__ __forceinline__ void fwd_exp_use(const f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4],
+                                            int v) {
+  const int n = v / 16, r = v % 16;
+  if (r < 4)
+    ls[n][r] = sj[n][r];
+  else
+    ls[n][r & 3] += sj[n][r];
+  asm volatile("" : "+v"(ls[n][r & 3]));
+  if (r % 8 == 7) {
+    pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
+    asm volatile("" : "+v"(pj[n][r / 8]));
+  }
+}
+
+// Exponential v of block j's scores, in place, and its uses: those of v - 1 when they
+// are pinned (a step apart, so no use waits on the transcendental result, which needs a
+// wait state; the phase then ends with fwd_exp_use of its last value), else its own.
 template <int QB>
 __device__ __forceinline__ void fwd_exp_one(f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4],
                                             const float (&nb)[QB], float c, int v) {
@@ -175,8 +202,17 @@ __device__ __forceinline__ void fwd_exp_one(f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2
   // towards its first use, out of the matrix-pipe phase it is meant to overlap.
   asm volatile("" : "+v"(e));
   sj[n][r] = e;
-  ls[n][r & 3] += e;
-  if (r % 8 == 7) pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
+  if constexpr (fwd_pin_uses<QB>()) {
+    if (v > 0) fwd_exp_use<QB>(sj, pj, ls, v - 1);
+  } else {
+    ls[n][r & 3] += e;
+    if (r % 8 == 7) pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
+  }
+}
+
+template <int QB>
+__device__ __forceinline__ void fwd_exp_end(const f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4]) {
+  if constexpr (fwd_pin_uses<QB>()) fwd_exp_use<QB>(sj, pj, ls, 16 * QB - 1);
 }
 
 template <int QB>
@@ -185,7 +221,7 @@ __device__ __forceinline__ void fwd_exp_begin(const float (&m_run)[QB], float c,
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     nb[n] = m_run[n] == -INFINITY ? 0.f : -m_run[n] * c;
-    ls[n][0] = ls[n][1] = ls[n][2] = ls[n][3] = 0.f;
+    if constexpr (!fwd_pin_uses<QB>()) ls[n][0] = ls[n][1] = ls[n][2] = ls[n][3] = 0.f;
   }
 }
 
@@ -237,6 +273,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
       for (int u = 0; u < E / NS; ++u) fwd_exp_one<QB>(s0, p0, ls, nb, c, s * (E / NS) + u);
       step_fence();
     }
+    fwd_exp_end<QB>(s0, p0, ls);
   }
 #pragma unroll
   for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
@@ -259,6 +296,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
       for (int u = 0; u < E / TP; ++u) fwd_exp_one<QB>(s1, p1, ls, nb, c, i * (E / TP) + u);
       step_fence();
     }
+    fwd_exp_end<QB>(s1, p1, ls);
   }
 #pragma unroll
   for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
