@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 746368789, "fetch_kib": 297881.6, "write_kib": 133123.8,
+    ("c3", "fwd"): {"bytes": 751943417, "fetch_kib": 300602.5, "write_kib": 133126.1,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
+                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 274770594, "fetch_kib": 132119.8, "write_kib": 4096.0,
+    ("c3", "bwd_preprocess"): {"bytes": 274770519, "fetch_kib": 132119.8, "write_kib": 4096.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
+                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 908041041, "fetch_kib": 310456.8, "write_kib": 265857.0,
+    ("c3", "bwd_dkdv"): {"bytes": 903830358, "fetch_kib": 308109.4, "write_kib": 266439.6,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
+                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 879553171, "fetch_kib": 363901.3, "write_kib": 131149.7,
+    ("c3", "bwd_dq"): {"bytes": 902061168, "fetch_kib": 374895.9, "write_kib": 131141.5,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a3c950384ee4b5749849df8f50b638de199f169696ea1f932813844b6bf29927",
+                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
