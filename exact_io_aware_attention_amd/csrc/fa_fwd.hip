@@ -50,6 +50,7 @@ template <int QB> constexpr int fwd_waves() { return 4; }
 template <int QB> constexpr int fwd_occupancy() { return QB == 1 ? 2 : 1; }
 constexpr int kFwdBC = 64;        // keys per tile
 constexpr float kRescaleTau = 8.f;  // log2 growth of the row max tolerated before rescaling
+constexpr float kKeepSum = 256.f;  // 2^tau: bound on a lane's share of a block's row sum (one block per wave)
 
 template <int D>
 struct FwdLds {
@@ -225,10 +226,171 @@ __device__ __forceinline__ void fwd_exp_begin(const float (&m_run)[QB], float c,
   }
 }
 
+// ---- One query block per wave (d = 128): the row-sum check instead of row maxima.
+// The exponentials of a 32-key block are formed under the current reference without
+// looking for the block's maximum first, and kept when every lane's share of each row sum
+// is at most 2^tau: then so is every single P, whatever the block's true maximum, which
+// is all the lazy rescale needs (O and l on one common reference, nothing overflows).
+// Only before a query's first visible key, or when the check fails, does the reference
+// move to the block's exact maximum and the exponentials get formed again. The row sums
+// are formed anyway, so the common case trades a 16-value maximum, a lane swap and a
+// serial section per block for one compare. (With two blocks per wave the raw scores that
+// the uncommon path needs cost more than this saves.)
+
+__device__ __forceinline__ float row_max16(const f32x16& x) {
+  float mx = x[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+  return mx;
+}
+
+// Hide the scores of block j (keys kb0 .. kb0 + 31) that the query does not see.
+template <bool CAUSAL>
+__device__ __forceinline__ void fwd1_mask(f32x16& sj, int kb0, int len, int wq0, int lane) {
+  const int qi = wq0 + (lane & 31), g = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kb0 + crow_nat(r, g);
+    sj[r] = (key >= len || (CAUSAL && key > qi)) ? -INFINITY : sj[r];
+  }
+}
+
+// Exponential r of the block (the raw scores stay), its share of the row sum and, every
+// eighth, the bf16 conversion of eight of them into P.
+__device__ __forceinline__ void fwd1_exp_one(const f32x16& sj, f32x8& ev, bf16x8 (&pj)[2], float (&ls)[4], float nb,
+                                             float c, int r) {
+  float e = fast_exp2(fmaf(sj[r], c, nb));
+  // Pin the exponential (and below the conversion) to this step: the compiler would sink
+  // them out of the matrix-pipe phase they are meant to overlap.
+  asm volatile("" : "+v"(e));
+  ev[r & 7] = e;
+  ls[r & 3] += e;
+  if (r % 8 == 7) {
+    pj[r / 8] = to_bf16x8(ev);
+    asm volatile("" : "+v"(pj[r / 8]));
+  }
+}
+
+// Whether the block's exponentials stand (see above); decided for the whole wave.
+__device__ __forceinline__ bool fwd1_keep(float m_run, const f32x16& sj, float bsum) {
+  bool redo = !(bsum <= kKeepSum);
+  if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0)  // before some query's first visible key
+    redo |= m_run == -INFINITY && row_max16(sj) > -INFINITY;
+  return __builtin_amdgcn_ballot_w64(redo) == 0;
+}
+
+// The uncommon path: the reference moves to the block's exact row maximum, l and O
+// (which holds only products formed under the old reference) are scaled to match, and
+// the block's exponentials are formed again.
+template <int D>
+__device__ __forceinline__ void fwd1_redo(FwdState<D, 1>& st, const f32x16& sj, bf16x8 (&pj)[2], float& bsum,
+                                          float c) {
+  const float m_new = fmaxf(st.m_run[0], pair_max(row_max16(sj)));
+  const float m_to = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2((st.m_run[0] - m_to) * c);
+  st.m_run[0] = m_new;
+  st.l_run[0] *= alpha;
+#pragma unroll
+  for (int bb = 0; bb < D / 32; ++bb) st.oacc[0][bb] *= alpha;
+  const float nb = -m_to * c;
+  f32x8 ev;
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    ev[r & 7] = fast_exp2(fmaf(sj[r], c, nb));
+    sum += ev[r & 7];
+    if (r % 8 == 7) pj[r / 8] = to_bf16x8(ev);
+  }
+  bsum = sum;
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, const u16* Vs, int k0, int len,
+                                            int wq0, int lane, float c, bool mask) {
+  constexpr int NS = D / 16, NB = D / 32;
+  constexpr int TP = 2 * NB;  // PV steps per key block
+  static_assert(16 % NS == 0 && 16 % TP == 0, "exponentials must split evenly over the steps");
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // S_0
+  {
+    bf16x8 a[NS];
+#pragma unroll
+    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 0, s, lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 0, s + kFwdPf, lane);
+      s0 = mfma32(a[s], st.qf[0][s], s0);
+      step_fence();
+    }
+  }
+  if (mask) fwd1_mask<CAUSAL>(s0, k0, len, wq0, lane);  // wave-uniform: a diagonal or tail tile
+
+  // S_1 with exp(S_0)
+  bf16x8 p0[2], p1[2];
+  f32x8 ev;
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  float nb = st.m_run[0] == -INFINITY ? 0.f : -st.m_run[0] * c;
+  {
+    bf16x8 a[NS];
+#pragma unroll
+    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 1, s, lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 1, s + kFwdPf, lane);
+      s1 = mfma32(a[s], st.qf[0][s], s1);
+#pragma unroll
+      for (int u = 0; u < 16 / NS; ++u) fwd1_exp_one(s0, ev, p0, ls, nb, c, s * (16 / NS) + u);
+      step_fence();
+    }
+  }
+  float bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  if (!fwd1_keep(st.m_run[0], s0, bsum)) fwd1_redo<D>(st, s0, p0, bsum, c);
+  st.l_run[0] += bsum;
+  if (mask) fwd1_mask<CAUSAL>(s1, k0 + 32, len, wq0, lane);
+
+  // P_0 V_0 with exp(S_1). If block 1 then moves the reference, P_0 (formed under the
+  // old one) has joined O already and is scaled with the rest of it.
+  ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
+  nb = st.m_run[0] == -INFINITY ? 0.f : -st.m_run[0] * c;
+  {
+    bf16x8 a[TP];
+#pragma unroll
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, i & 1, lane);
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, (i + kFwdPf) & 1, lane);
+      st.oacc[0][i >> 1] = mfma32(a[i], p0[i & 1], st.oacc[0][i >> 1]);
+#pragma unroll
+      for (int u = 0; u < 16 / TP; ++u) fwd1_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
+      step_fence();
+    }
+  }
+  bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  if (!fwd1_keep(st.m_run[0], s1, bsum)) fwd1_redo<D>(st, s1, p1, bsum, c);
+  st.l_run[0] += bsum;
+
+  // P_1 V_1
+  {
+    bf16x8 a[TP];
+#pragma unroll
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, 2 + (i & 1), lane);
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, 2 + ((i + kFwdPf) & 1), lane);
+      st.oacc[0][i >> 1] = mfma32(a[i], p1[i & 1], st.oacc[0][i >> 1]);
+      step_fence();
+    }
+  }
+}
+
 // One key tile for one wave: S^T = K Q^T, softmax update, O^T += V^T P^T.
 template <int D, int QB, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
                                          int wq0, int lane, float c, bool mask) {
+  if constexpr (QB == 1) {
+    fwd_tile_q1<D, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, c, mask);
+    return;
+  }
   constexpr int NS = D / 16, NB = D / 32, E = 16 * QB;
   constexpr int TP = 2 * NB;  // PV steps per key block: (bb, t) for t in the block's two slices
   static_assert(E % NS == 0 && E % TP == 0, "exponentials must split evenly over the steps");
