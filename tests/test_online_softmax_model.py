@@ -98,3 +98,70 @@ def test_tiled_model_equals_oracle(causal, n, br, bc, threshold):
     g = tiled_backward(q, k, v, do, o, lse, scale, causal, br, bc)
     for a, b in zip(g, g_ref):
         np.testing.assert_allclose(a, b, atol=1e-11)
+
+
+# Keys of a 32-key block held by lane half g (the MFMA output layout: row 8(r/4) + 4g +
+# r % 4 of register r), whose exponentials form one lane's share of the row sum.
+_HALF_KEYS = [np.array([8 * (r // 4) + 4 * g + r % 4 for r in range(16)]) for g in (0, 1)]
+
+
+def tiled_forward_sumcheck(q, k, v, scale, causal, br, keep=256.0):
+    """The forward with one 32-query block per wave: per 32-key block, exponentials under
+    the current reference are kept when every lane's share of the row sum is at most
+    `keep` (= 2^8) for every row of the wave; otherwise, and while some row of the wave
+    has no reference yet but sees a key of the block, the reference moves to the block's
+    exact row maximum first. Returns O, LSE and the largest P ever formed."""
+    n, d = q.shape
+    c = scale * LOG2E
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    p_max = 0.0
+    for i0 in range(0, n, br):
+        rows = np.arange(i0, min(n, i0 + br))
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        acc = np.zeros((len(rows), v.shape[1]))
+        for j0 in range(0, n, 32):
+            cols = np.arange(j0, j0 + 32)
+            valid = cols < n
+            s = np.full((len(rows), 32), -np.inf)
+            s[:, valid] = q[rows] @ k[cols[valid]].T
+            if causal:
+                s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+            nb = np.where(np.isfinite(m), -m * c, 0.0)
+            with np.errstate(over="ignore", invalid="ignore"):
+                p = np.exp2(s * c + nb[:, None])
+            shares = np.stack([p[:, h].sum(axis=1) for h in _HALF_KEYS])
+            redo = not np.all(shares <= keep)
+            redo |= bool(np.any(~np.isfinite(m) & (s.max(axis=1) > -np.inf)))
+            if redo:
+                m_new = np.maximum(m, s.max(axis=1))
+                m_to = np.where(np.isfinite(m_new), m_new, 0.0)
+                alpha = np.where(np.isfinite(m), np.exp2((m - m_to) * c), 0.0)
+                l, acc, m = alpha * l, alpha[:, None] * acc, m_new
+                p = np.exp2(s * c - (m_to * c)[:, None])
+            p_max = max(p_max, float(p.max()))
+            l = l + p.sum(axis=1)
+            acc = acc + p[:, valid] @ v[cols[valid]]
+        o[rows] = acc / l[:, None]
+        lse[rows] = scale * m + np.log(l)
+    return o, lse, p_max
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 31, 64, 97])
+@pytest.mark.parametrize("growth", [0.0, 0.6])
+def test_sumcheck_model_equals_oracle(causal, n, growth):
+    """Exact (to fp64 rounding) with random scores, and with scores that grow along the
+    keys (growth > 0: every later block exceeds the reference, so the uncommon path runs
+    again and again); no P ever exceeds 2^8."""
+    rng = np.random.default_rng(n + int(10 * growth))
+    d = 16
+    q, k, v = (rng.standard_normal((n, d)) * 2.0 for _ in range(3))
+    k = k + growth * np.arange(n)[:, None] * np.sign(q.mean(axis=0))[None, :]
+    scale = 1 / math.sqrt(d)
+    o_ref, lse_ref = oracle.head_forward(q, k, v, scale, causal)
+    o, lse, p_max = tiled_forward_sumcheck(q, k, v, scale, causal, br=32)
+    np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-10)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-10, rtol=1e-12)
+    assert p_max <= 256.0
