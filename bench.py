@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 751943417, "fetch_kib": 300602.5, "write_kib": 133126.1,
+    ("c3", "fwd"): {"bytes": 745814104, "fetch_kib": 297607.1, "write_kib": 133131.1,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
+                  "sources_sha256": "73316242989cc2862f3ff655266e331b6d97638ef2f724cf3ac4eb61d446a644",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 274770519, "fetch_kib": 132119.8, "write_kib": 4096.0,
+    ("c3", "bwd_preprocess"): {"bytes": 274770647, "fetch_kib": 132119.8, "write_kib": 4096.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
+                  "sources_sha256": "73316242989cc2862f3ff655266e331b6d97638ef2f724cf3ac4eb61d446a644",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 903830358, "fetch_kib": 308109.4, "write_kib": 266439.6,
+    ("c3", "bwd_dkdv"): {"bytes": 903891339, "fetch_kib": 308221.8, "write_kib": 266274.4,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
+                  "sources_sha256": "73316242989cc2862f3ff655266e331b6d97638ef2f724cf3ac4eb61d446a644",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 902061168, "fetch_kib": 374895.9, "write_kib": 131141.5,
+    ("c3", "bwd_dq"): {"bytes": 904068241, "fetch_kib": 375822.4, "write_kib": 131248.4,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "60e54c69c95edb0b4e0731b4e863f29d47691e55f8856ab7cca8dc4d76a53529",
+                  "sources_sha256": "73316242989cc2862f3ff655266e331b6d97638ef2f724cf3ac4eb61d446a644",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
