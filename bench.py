@@ -270,7 +270,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (not varlen)")
