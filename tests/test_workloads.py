@@ -48,3 +48,21 @@ def test_sample_rows():
     r = W.sample_rows(7, 65536, 256)
     assert len(r) == 256 and len(set(r.tolist())) == 256 and np.all(np.diff(r) > 0)
     assert np.array_equal(r, W.sample_rows(7, 65536, 256))
+
+
+def test_device_tensors_are_seeded_and_rounded():
+    """make_device_tensors (used for multi-GiB inputs): same seed, same values; tensor i
+    uses seed + i; values are the fp32 normals times std rounded to the storage dtype
+    (E4M3 codes for uint8)."""
+    a1, b1 = W.make_device_tensors((4, 300, 3, 8), 2, seed=9, std=0.5, dtype=torch.bfloat16, device="cpu")
+    a2, = W.make_device_tensors((4, 300, 3, 8), 1, seed=9, std=0.5, dtype=torch.bfloat16, device="cpu")
+    b2, = W.make_device_tensors((4, 300, 3, 8), 1, seed=10, std=0.5, dtype=torch.bfloat16, device="cpu")
+    assert a1.dtype == torch.bfloat16 and a1.shape == (4, 300, 3, 8)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2) and not torch.equal(a1, b1)
+    g = torch.Generator(device="cpu").manual_seed(9)
+    ref = (torch.randn(a1.numel(), generator=g, dtype=torch.float32) * 0.5).to(torch.bfloat16)
+    assert torch.equal(a1.flatten(), ref)
+    c, = W.make_device_tensors((1000,), 1, seed=3, std=2.0, dtype=torch.uint8, device="cpu")
+    g = torch.Generator(device="cpu").manual_seed(3)
+    ref8 = (torch.randn(1000, generator=g, dtype=torch.float32) * 2.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert c.dtype == torch.uint8 and torch.equal(c, ref8)

@@ -267,3 +267,27 @@ def make_fp8_inputs(w: Fp8Workload, seed: Optional[int] = None, *, batch: Option
         x = torch.randn((B, N, H, d), generator=g, dtype=torch.float32) * (w.std / ds)
         out.append(x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
     return tuple(out)
+
+
+def make_device_tensors(shape, count: int, seed: int, std: float, dtype: torch.dtype,
+                        device="cuda") -> tuple:
+    """`count` seeded iid normal tensors of one shape generated on the device (for
+    inputs of several GiB, where host generation is slow): tensor i is torch.randn from
+    a device generator seeded seed + i, times std, rounded to `dtype` (RNE; for
+    torch.uint8 the values are rounded to E4M3 by torch's float8_e4m3fn conversion and
+    returned as their codes). Built 2^26 elements at a time, so the fp32 temporary stays
+    small."""
+    n = math.prod(shape)
+    chunk = 1 << 26
+    out = []
+    for i in range(count):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed + i)
+        t = torch.empty(n, device=device, dtype=dtype)
+        for a in range(0, n, chunk):
+            x = torch.randn(min(chunk, n - a), generator=g, device=device, dtype=torch.float32)
+            if std != 1.0:
+                x.mul_(std)
+            t[a:a + x.numel()] = x.to(torch.float8_e4m3fn).view(torch.uint8) if dtype == torch.uint8 else x.to(dtype)
+        out.append(t.view(shape))
+    return tuple(out)
