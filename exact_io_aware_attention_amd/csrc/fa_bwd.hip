@@ -557,22 +557,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
     kv_acc_fence<D>(st.dvT[bb]);
     kv_acc_fence<D>(st.dkT[bb]);
   }
-  if (kj >= len) return;
-  u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
-  u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
-  const float nscale = -p.scale;  // the accumulator holds -dK^T / scale
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
-      const int col = 32 * bb + 8 * a + 4 * g;
-      store_bf16x4(dKg + col, st.dkT[bb][4 * a] * nscale, st.dkT[bb][4 * a + 1] * nscale,
-                   st.dkT[bb][4 * a + 2] * nscale, st.dkT[bb][4 * a + 3] * nscale);
-      store_bf16x4(dVg + col, st.dvT[bb][4 * a], st.dvT[bb][4 * a + 1], st.dvT[bb][4 * a + 2],
-                   st.dvT[bb][4 * a + 3]);
-    }
-  }
+  // Every wave is past its last tile read: the LDS now stages this wave's dK and dV rows
+  // (32 keys each) so that they leave as whole rows.
+  static_assert(kKvWaves * 64 * stage_pitch<D>() <= S * L::BUF, "staging fits in the tile buffers");
+  lds_barrier();
+  u16* stg = lds + w * 64 * stage_pitch<D>();
+  stage_acc_rows<D>(stg, st.dkT, -p.scale, lr, g);  // the accumulator holds -dK^T / scale
+  stage_acc_rows<D>(stg + 32 * stage_pitch<D>(), st.dvT, 1.f, lr, g);
+  const int valid = len - wk0;
+  store_staged_rows<D, 32>(stg, p.dk + base + (size_t)wk0 * stride, stride, valid, lane);
+  store_staged_rows<D, 32>(stg + 32 * stage_pitch<D>(), p.dv + base + (size_t)wk0 * stride, stride, valid, lane);
 }
 
 // ------------------------------------------------------------------------ bwd_dkdv, head_dim 64
@@ -832,21 +826,17 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_rows_kernel(BwdParams 
     kv_acc_fence<D>(st.dvT[bb]);
     kv_acc_fence<D>(st.dkT[bb]);
   }
-  if (kj >= len) return;
-  u16* __restrict__ dKg = p.dk + base + (size_t)kj * stride;
-  u16* __restrict__ dVg = p.dv + base + (size_t)kj * stride;
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
-      const int col = 32 * bb + 8 * a + 4 * g;
-      store_bf16x4(dKg + col, st.dkT[bb][4 * a] * p.scale, st.dkT[bb][4 * a + 1] * p.scale,
-                   st.dkT[bb][4 * a + 2] * p.scale, st.dkT[bb][4 * a + 3] * p.scale);
-      store_bf16x4(dVg + col, st.dvT[bb][4 * a], st.dvT[bb][4 * a + 1], st.dvT[bb][4 * a + 2],
-                   st.dvT[bb][4 * a + 3]);
-    }
-  }
+  // buf0 stages this wave's dK rows, then its dV rows, so that they leave as whole rows;
+  // the three-buffer loop leaves right after its last tile, so every wave must be past
+  // its reads of the tiles first.
+  static_assert(kKvWaves * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
+  lds_barrier();
+  u16* stg = buf0 + w * 32 * stage_pitch<D>();
+  const int valid = len - wk0;
+  stage_acc_rows<D>(stg, st.dkT, p.scale, lr, g);
+  store_staged_rows<D, 32>(stg, p.dk + base + (size_t)wk0 * stride, stride, valid, lane);
+  stage_acc_rows<D>(stg, st.dvT, 1.f, lr, g);
+  store_staged_rows<D, 32>(stg, p.dv + base + (size_t)wk0 * stride, stride, valid, lane);
 }
 
 // ------------------------------------------------------------------------ bwd_dq
@@ -1007,17 +997,13 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
     __syncthreads();
   }
 
-  if (qi >= len) return;
-  u16* __restrict__ dQg = p.dq + base + (size_t)qi * stride;
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int col = 32 * bb + 8 * a + 4 * g;
-      store_bf16x4(dQg + col, st.dqT[bb][4 * a] * p.scale, st.dqT[bb][4 * a + 1] * p.scale,
-                   st.dqT[bb][4 * a + 2] * p.scale, st.dqT[bb][4 * a + 3] * p.scale);
-    }
-  }
+  // The tiles are consumed (the loop ends on a barrier): buf1 stages this wave's dQ rows
+  // so that they leave as whole rows (buf1, since a workgroup's next query tile starts
+  // by copying into buf0; its first barrier comes after these reads).
+  static_assert(4 * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
+  u16* stg = buf1 + w * 32 * stage_pitch<D>();
+  stage_acc_rows<D>(stg, st.dqT, p.scale, lr, g);
+  store_staged_rows<D, 32>(stg, p.dq + base + (size_t)wq0 * stride, stride, len - wq0, lane);
 #endif
 }
 

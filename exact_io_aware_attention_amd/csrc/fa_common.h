@@ -97,6 +97,43 @@ __device__ __forceinline__ void store_bf16x4(u16* dst, float a, float b, float c
   *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(f32x4{a, b, c, d}, bf16x4);
 }
 
+// Output rows leave through LDS so that each row is written whole. The lane holding
+// row lr (0..31) in lane group g has head-dim entries 32 bb + 8 a + 4 g + {0..3} of
+// accumulator bb in its registers 4a..4a+3 (the C layout of a 32x32 MFMA with one row
+// per column lane); stored directly, every store instruction would put 8 bytes into
+// each of 32 rows. Staged as bf16 rows (pitch D + 8 elements: 16-byte aligned rows), the
+// tile is read back so that D / 8 lanes write one row with 16-byte stores.
+template <int D>
+constexpr int stage_pitch() { return D + 8; }
+
+template <int D>
+__device__ __forceinline__ void stage_acc_rows(u16* stg, const f32x16 (&acc)[D / 32], float mul, int lr, int g) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<bf16x4*>(stg + lr * stage_pitch<D>() + 32 * bb + 8 * a + 4 * g) = __builtin_convertvector(
+          f32x4{acc[bb][4 * a] * mul, acc[bb][4 * a + 1] * mul, acc[bb][4 * a + 2] * mul, acc[bb][4 * a + 3] * mul},
+          bf16x4);
+}
+
+// Writes staged rows 0 .. ROWS-1 that are below `valid`: row r goes to dst + r * stride
+// (16-byte aligned rows of D bf16).
+template <int D, int ROWS>
+__device__ __forceinline__ void store_staged_rows(const u16* stg, u16* __restrict__ dst, size_t stride, int valid,
+                                                  int lane) {
+  constexpr int LPR = D / 8, RPI = 64 / LPR;  // lanes per row, rows per store instruction
+  static_assert(ROWS % RPI == 0, "whole store instructions");
+  const int c = lane % LPR, r0 = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < ROWS / RPI; ++i) {
+    const int r = RPI * i + r0;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * stage_pitch<D>() + 8 * c);
+    if (r < valid) *reinterpret_cast<u32x4*>(dst + (size_t)r * stride + 8 * c) = v;
+  }
+}
+
 __device__ __forceinline__ f32x8 half_of(const f32x16& x, int h) {
   return h == 0 ? f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]}
                 : f32x8{x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]};

@@ -559,27 +559,18 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
   for (int n = 0; n < QB; ++n)
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) fwd_o_fence<QB>(st.oacc[n][bb]);
+  // The tiles are consumed (the loop ends on a barrier): buf1 stages each 32-query block
+  // of O so that its rows leave whole (buf1, since a workgroup's next query tile starts by
+  // copying into buf0; its first barrier comes after these reads).
+  static_assert(NW * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
+  u16* stg = buf1 + w * 32 * stage_pitch<D>();
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
     const float l_tot = pair_sum(st.l_run[n]);
-    if (qi >= len) continue;
-    const float inv = 1.f / l_tot;
-    u16* __restrict__ Og = p.o + base + (size_t)qi * stride;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float x0 = st.oacc[n][bb][4 * a] * inv, x1 = st.oacc[n][bb][4 * a + 1] * inv;
-        const float x2 = st.oacc[n][bb][4 * a + 2] * inv, x3 = st.oacc[n][bb][4 * a + 3] * inv;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        typedef float f32x4_ __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<bf16x4*>(Og + 32 * bb + 8 * a + 4 * g) =
-            __builtin_convertvector(f32x4_{x0, x1, x2, x3}, bf16x4);
-      }
-    }
-    if (g == 0) {
+    stage_acc_rows<D>(stg, st.oacc[n], 1.f / l_tot, lr, g);
+    store_staged_rows<D, 32>(stg, p.o + base + (size_t)(wq0 + 32 * n) * stride, stride, len - (wq0 + 32 * n), lane);
+    if (g == 0 && qi < len) {
       const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
       p.lse[li] = st.m_run[n] * p.scale + logf(l_tot);
     }

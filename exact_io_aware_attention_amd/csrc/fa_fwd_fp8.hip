@@ -240,21 +240,16 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(Fp8Params p) {
     __syncthreads();
   }
 
-  if (qi >= len) return;
+  // The tiles are consumed (the loop ends on a barrier): the two buffers stage the O rows
+  // (waves 0, 1 in buf0, waves 2, 3 in buf1) so that they leave whole. O rows are D bf16
+  // apart by token (stride counts the 8-bit inputs' bytes).
+  constexpr int SROWS = 32 * stage_pitch<D>();  // u16 elements of one wave's staging
+  static_assert(2 * SROWS * 2 <= L::BUF, "two waves' staging fits in one tile buffer");
+  u16* stg = reinterpret_cast<u16*>(w < 2 ? buf0 : buf1) + (w & 1) * SROWS;
   const float l_tot = pair_sum(st.l_run);
-  const float inv = p.descale_v / l_tot;
-  u16* __restrict__ Og = p.o + (base + (size_t)qi * stride);  // O rows are D bf16 apart by token
-#pragma unroll
-  for (int mt = 0; mt < NM; ++mt) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      // lane group g holds head-dim entries 32mt + 8a + 4g + {0..3} in registers 4a..4a+3
-      const int col = 32 * mt + 8 * a + 4 * g;
-      store_bf16x4(Og + col, st.oacc[mt][4 * a] * inv, st.oacc[mt][4 * a + 1] * inv,
-                   st.oacc[mt][4 * a + 2] * inv, st.oacc[mt][4 * a + 3] * inv);
-    }
-  }
-  if (g == 0) p.lse[((size_t)b * p.H + h) * p.N + qi] = st.m_ref * p.scale_eff + logf(l_tot);
+  stage_acc_rows<D>(stg, st.oacc, p.descale_v / l_tot, lr, g);
+  store_staged_rows<D, 32>(stg, p.o + base + (size_t)wq0 * stride, stride, len - wq0, lane);
+  if (g == 0 && qi < len) p.lse[((size_t)b * p.H + h) * p.N + qi] = st.m_ref * p.scale_eff + logf(l_tot);
 #endif
 }
 
