@@ -559,17 +559,30 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
   for (int n = 0; n < QB; ++n)
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) fwd_o_fence<QB>(st.oacc[n][bb]);
-  // The tiles are consumed (the loop ends on a barrier): buf1 stages each 32-query block
-  // of O so that its rows leave whole (buf1, since a workgroup's next query tile starts by
-  // copying into buf0; its first barrier comes after these reads).
+  // With one query block per wave, the tiles being consumed (the loop ends on a barrier),
+  // buf1 stages O so that its rows leave whole (buf1, since a workgroup's next query tile
+  // starts by copying into buf0; its first barrier comes after these reads). With two,
+  // the O accumulators sit in AGPRs and staging cost the tile loop registers (measured
+  // slower at long sequences), so those rows are stored directly.
   static_assert(NW * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
   u16* stg = buf1 + w * 32 * stage_pitch<D>();
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
     const float l_tot = pair_sum(st.l_run[n]);
-    stage_acc_rows<D>(stg, st.oacc[n], 1.f / l_tot, lr, g);
-    store_staged_rows<D, 32>(stg, p.o + base + (size_t)(wq0 + 32 * n) * stride, stride, len - (wq0 + 32 * n), lane);
+    if constexpr (QB == 1) {
+      stage_acc_rows<D>(stg, st.oacc[n], 1.f / l_tot, lr, g);
+      store_staged_rows<D, 32>(stg, p.o + base + (size_t)wq0 * stride, stride, len - wq0, lane);
+    } else if (qi < len) {
+      const float inv = 1.f / l_tot;
+      u16* __restrict__ Og = p.o + base + (size_t)qi * stride;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)  // lane group g: head-dim entries 32bb + 8a + 4g + {0..3}
+          store_bf16x4(Og + 32 * bb + 8 * a + 4 * g, st.oacc[n][bb][4 * a] * inv, st.oacc[n][bb][4 * a + 1] * inv,
+                       st.oacc[n][bb][4 * a + 2] * inv, st.oacc[n][bb][4 * a + 3] * inv);
+    }
     if (g == 0 && qi < len) {
       const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
       p.lse[li] = st.m_run[n] * p.scale + logf(l_tot);
