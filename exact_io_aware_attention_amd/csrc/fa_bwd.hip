@@ -419,14 +419,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int wk0 = k0 + 32 * w;  // first key of this wave
   const int kj = wk0 + lr;      // this lane's key
 
-  KvState<D> st;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const size_t off = base + (size_t)kj * stride + 16 * s + 8 * g;
-    st.kf[s] = kj < len ? ld16(p.k + off) : zero_bf16x8();
-    const bf16x8 v = kj < len ? ld16(p.v + off) : zero_bf16x8();
-    st.vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);
-  }
+  KvState<D> st;  // K and V rows are read in the prologue
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
     st.dvT[bb] = f32x16{};
@@ -474,18 +467,34 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
       wait_vmem();
   };
 
-  // Prologue: tiles qt_begin .. qt_begin + S - 2 in flight; wait for the first.
-  static_assert(S == 3 || S == 4, "two or three tiles ahead");
+  // Prologue. This key tile's K and V rows come in through LDS buffers 2 and 3, whole
+  // rows per copy instruction (loaded straight into registers, every load instruction
+  // would gather 32 bytes from each of 32 rows), while tiles qt_begin and qt_begin + 1
+  // land in buffers 0 and 1. Every wave takes its rows into registers before tile
+  // qt_begin + 2 refills buffer 2; tile qt_begin + 3 goes to buffer 3 after the barrier
+  // of tile qt_begin.
+  static_assert(S == 4, "the K/V rows pass through buffers 2 and 3");
+  constexpr int KVP = D + 8;  // row pitch of the staged K/V rows: conflict-free row reads
+  static_assert(BK * KVP <= L::BUF, "a K or V tile fits in one buffer");
+  {
+    TileDma<BK, D, KVP, kKvWaves> kvdma;
+    kvdma.init(stride, w, lane);
+    kvdma.issue(lds + 2 * L::BUF, p.k + base, k0, len, stride, w, lane);
+    kvdma.issue(lds + 3 * L::BUF, p.v + base, k0, len, stride, w, lane);
+  }
   issue(qt_begin);
+  if (qt_begin + 1 < n_qt) issue(qt_begin + 1);
+  wait_vmem();
+  lds_barrier();
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    settle(st.kf[s]);
-    settle(st.vf[s]);
+    const int e = (32 * w + lr) * KVP + 16 * s + 8 * g;  // this lane's key row, head-dim 16 s + 8 g
+    st.kf[s] = kj < len ? ld16(lds + 2 * L::BUF + e) : zero_bf16x8();
+    const bf16x8 v = kj < len ? ld16(lds + 3 * L::BUF + e) : zero_bf16x8();
+    st.vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);
   }
-  for (int i = 1; i < S - 1; ++i)
-    if (qt_begin + i < n_qt) issue(qt_begin + i);
-  wait_tiles(min(S - 2, n_qt - qt_begin - 1));
   lds_barrier();
+  if (qt_begin + 2 < n_qt) issue(qt_begin + 2);
 
   KvBlock blk0, blk1;
   bf16x8 rop[kKvPf], top[kKvPf], pb[2], db[2];
