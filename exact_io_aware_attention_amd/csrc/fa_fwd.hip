@@ -507,9 +507,10 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
 #pragma unroll
   for (int n = 0; n < QB; ++n) {
     const int qi = wq0 + 32 * n + lr;
+    if constexpr (QB != 1)  // one block per wave: Q comes in through LDS below
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      st.qf[n][s] = qi < len ? ld16(Qg + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
+      for (int s = 0; s < NS; ++s)
+        st.qf[n][s] = qi < len ? ld16(Qg + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) st.oacc[n][bb] = f32x16{};
     st.m_run[n] = -INFINITY;
@@ -536,13 +537,35 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
     }
   };
   // Two LDS buffers in turn: the copy of tile kt+1 is in flight while tile kt is used.
-  issue(0, buf0);
+  if constexpr (QB == 1) {
+    // The tile's Q rows come in through buf1 (whole-row copies; loaded straight into
+    // registers, every load instruction would gather 32 bytes from each of 32 rows) while
+    // K/V tile 0 lands in buf0; every wave takes its rows before tile 1 refills buf1.
+    // The first barrier lets every wave finish reading the previous query tile's O rows
+    // out of buf1.
+    constexpr int QP = D + 8;  // row pitch of the staged Q rows: conflict-free row reads
+    static_assert(BR * QP <= L::BUF, "the Q tile fits in one buffer");
+    __syncthreads();
+    TileDma<BR, D, QP, NW> qdma;
+    qdma.init(stride, w, lane);
+    qdma.issue(buf1, Qg, q0, len, stride, w, lane);
+    issue(0, buf0);
+    wait_vmem();
+    __syncthreads();
+    const int qi = wq0 + lr;
 #pragma unroll
-  for (int n = 0; n < QB; ++n)
+    for (int s = 0; s < NS; ++s)
+      st.qf[0][s] = qi < len ? ld16(buf1 + (32 * w + lr) * QP + 16 * s + 8 * g) : zero_bf16x8();
+    __syncthreads();
+  } else {
+    issue(0, buf0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) settle(st.qf[n][s]);
-  wait_vmem();
-  __syncthreads();
+    for (int n = 0; n < QB; ++n)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) settle(st.qf[n][s]);
+    wait_vmem();
+    __syncthreads();
+  }
   for (int kt = 0; kt < n_kt; kt += 2) {
     if (kt + 1 < n_kt) issue(kt + 1, buf1);
     compute(kt, buf0);
