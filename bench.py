@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 731552730, "fetch_kib": 290649.0, "write_kib": 133120.0,
+    ("c3", "fwd"): {"bytes": 727180697, "fetch_kib": 288515.1, "write_kib": 133120.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "287b286de7f5c629c52086ada799c7cbece1d7a02ffd32560cd95a0eccab4e78",
+                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 274771159, "fetch_kib": 132120.1, "write_kib": 4096.0,
+    ("c3", "bwd_preprocess"): {"bytes": 274770352, "fetch_kib": 132120.1, "write_kib": 4096.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "287b286de7f5c629c52086ada799c7cbece1d7a02ffd32560cd95a0eccab4e78",
+                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 905216670, "fetch_kib": 310934.2, "write_kib": 262144.0,
+    ("c3", "bwd_dkdv"): {"bytes": 962260495, "fetch_kib": 338789.2, "write_kib": 262144.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "287b286de7f5c629c52086ada799c7cbece1d7a02ffd32560cd95a0eccab4e78",
+                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 896621782, "fetch_kib": 372274.6, "write_kib": 131072.0,
+    ("c3", "bwd_dq"): {"bytes": 903142509, "fetch_kib": 375459.8, "write_kib": 131072.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "287b286de7f5c629c52086ada799c7cbece1d7a02ffd32560cd95a0eccab4e78",
+                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
