@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   }
   issue(qt_begin);
   if (qt_begin + 1 < n_qt) issue(qt_begin + 1);
-  wait_vmem();
+  wait_tiles(min(1, n_qt - qt_begin - 1));  // the K/V rows and tile qt_begin (older copies)
   lds_barrier();
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
