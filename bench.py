@@ -43,21 +43,21 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
 # the value they had when the counters were taken; otherwise null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 727180697, "fetch_kib": 288515.1, "write_kib": 133120.0,
+    ("c3", "fwd"): {"bytes": 724759552, "fetch_kib": 287332.9, "write_kib": 133120.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
+                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 274770352, "fetch_kib": 132120.1, "write_kib": 4096.0,
+    ("c3", "bwd_preprocess"): {"bytes": 274770234, "fetch_kib": 132120.1, "write_kib": 4096.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
+                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 962260495, "fetch_kib": 338789.2, "write_kib": 262144.0,
+    ("c3", "bwd_dkdv"): {"bytes": 964896062, "fetch_kib": 340076.2, "write_kib": 262144.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
+                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 903142509, "fetch_kib": 375459.8, "write_kib": 131072.0,
+    ("c3", "bwd_dq"): {"bytes": 898215941, "fetch_kib": 373054.3, "write_kib": 131072.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "a00cbeddb914f358c5a02542ecca9a292fe431194bc1e92edfc93d83a02cfdfd",
+                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
