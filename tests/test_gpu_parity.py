@@ -55,6 +55,19 @@ def test_packed_parity(dtype, d, causal):
     full_parity(inp, causal, w.scale, dtype, f"packed {dtype} d{d} c{int(causal)}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_with_empty_sequences(dtype, d, causal):
+    """Zero-length sequences in a packed batch (first, between others, last) own no
+    tokens: every kernel skips them and the other sequences are unaffected."""
+    lengths = [0, 5, 0, 0, 130, 64, 0]
+    w = _w(dtype, d, causal)
+    inp = W.make_inputs(w, seed=3100 + d, heads=2, lengths=lengths)
+    assert inp.cu_seqlens.tolist() == [0, 0, 5, 5, 5, 135, 199, 199]
+    full_parity(inp, causal, w.scale, dtype, f"packed with empty {dtype} d{d} c{int(causal)}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_peaky_softmax(d, causal):
