@@ -35,6 +35,10 @@ METRIC = "attention fwd/bwd TFLOP/s, bf16 d=128 N=4096 causal; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA, published (twice bf16)
+BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 MFMA FLOP per clock per compute unit (gfx950)
+# The headline targets: the forward at >= 50 % and the backward at >= 35 % of the bf16
+# dense MFMA peak on the Llama-shaped causal workload.
+TARGET_FRAC = {"fwd": 0.50, "bwd": 0.35}
 CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 
 # HBM traffic per launch of a kernel, from two rocprofv3 --pmc passes over this script
@@ -62,20 +66,28 @@ TRAFFIC = {
 }
 
 
-def sources_sha256() -> str:
+# The sources each kernel is built from: its counters stay valid while these are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ("fa_fwd.hip", "fa_common.h", "fa_launch.h"),
+    "bwd_preprocess": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
+    "bwd_dq": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
+}
+
+
+def sources_sha256(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def traffic_for(workload: str, kernel: str):
     t = TRAFFIC.get((workload, kernel))
-    if t is None or t["sources_sha256"] != sources_sha256():
+    if t is None or kernel not in KERNEL_SOURCES or t["sources_sha256"] != sources_sha256(kernel):
         return None
     return t
 
@@ -189,7 +201,7 @@ def decode_bench(reps: int = 20):
     return res
 
 
-def fp8_bench(reps: int = 20):
+def fp8_bench(reps: int = 20, batch=None, seqlen=None):
     """fa_fwd_fp8 on the 8-bit workloads: median time of `reps` calls (HIP events on the
     launch stream) and the forward's algorithmic FLOPs (2 GEMM units, halved under causal)
     per second against the fp8 MFMA peak."""
@@ -198,7 +210,7 @@ def fp8_bench(reps: int = 20):
     import workloads as W
     res = {}
     for name, w in sorted(W.FP8_WORKLOADS.items()):
-        q8, k8, v8 = (t.cuda() for t in W.make_fp8_inputs(w))
+        q8, k8, v8 = (t.cuda() for t in W.make_fp8_inputs(w, batch=batch, seqlen=seqlen))
         B, N, H, d = q8.shape
         o = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16)
         lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
@@ -223,21 +235,81 @@ def fp8_bench(reps: int = 20):
         ms = sorted(ts)[len(ts) // 2]
         flops = 2 * (2.0 * B * H * N * N * d) * (0.5 if w.causal else 1.0)
         tf = flops / (ms * 1e-3) / 1e12
-        res[name] = {"workload": w.description, "batch": B, "heads": H, "seqlen": N, "head_dim": d,
+        res[name] = {"workload": w.description + (" (resized)" if batch or seqlen else ""),
+                     "batch": B, "heads": H, "seqlen": N, "head_dim": d,
                      "causal": w.causal, "ms": round(ms, 4), "tflops": round(tf, 2), "bound": "mfma",
                      "peak_tflops": PEAK_FP8_TFLOPS, "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
         del q8, k8, v8, o, lse
     return res
 
 
+def ceilings(reps: int = 5):
+    """The device's own figures and measured ceilings: compute units and maximum engine
+    clock as the HIP runtime reports them (the dense bf16 MFMA peak follows as CUs x 4096
+    FLOP/clk x clock), then three loops timed with HIP events on the launch stream (median
+    of `reps`): independent bf16 MFMA chains in every SIMD, independent v_exp_f32 and fp32
+    FMA chains in every lane (the vector-ALU roof of the softmax), and a 1 GiB copy."""
+    import torch
+    import exact_io_aware_attention_amd as fa
+    info = fa.fa_device_info(torch.cuda.current_device())
+    cus, clk_khz = info["compute_units"], info["max_clock_khz"]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    def ok(st, name):
+        if st != fa.FA_OK:
+            raise fa.FAError(st, name)
+
+    mblocks, miters = 4 * cus, 400          # four waves per SIMD, four chains per wave
+    vblocks, viters = 32 * cus, 1000
+    out = torch.empty(max(mblocks, vblocks) * 256, device="cuda", dtype=torch.float32)
+    t_mfma = timed(lambda: ok(fa.fa_ubench_mfma_bf16(out.data_ptr(), mblocks, miters, sp), "mfma"))
+    t_exp = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 0, sp), "exp"))
+    t_fma = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 1, sp), "fma"))
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: ok(fa.fa_ubench_copy(src.data_ptr(), dst.data_ptr(), nbytes, 16 * cus, sp), "copy"))
+    del src, dst, out
+    torch.cuda.empty_cache()
+    mfma_flops = mblocks * 4 * miters * 4 * 32768.0
+    lane_ops = vblocks * 256 * viters * 8.0
+    clk_hz = clk_khz * 1e3
+    return {
+        "device": info,
+        "peak_bf16_tflops_from_clock": round(cus * BF16_FLOP_PER_CLK_CU * clk_hz / 1e12, 1),
+        "mfma_bf16_loop_tflops": round(mfma_flops / (t_mfma * 1e-3) / 1e12, 1),
+        "exp_gops": round(lane_ops / (t_exp * 1e-3) / 1e9, 1),
+        "exp_lane_ops_per_clk_cu": round(lane_ops / (t_exp * 1e-3) / clk_hz / cus, 2),
+        "fma_fp32_tflops": round(2 * lane_ops / (t_fma * 1e-3) / 1e12, 1),
+        "fma_lane_ops_per_clk_cu": round(lane_ops / (t_fma * 1e-3) / clk_hz / cus, 2),
+        "copy_gbs": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+        "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4)},
+        "note": "rates per clock use the reported maximum clock; the clock under load may be lower",
+    }
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """Time the oracle (fp64, NumPy) on whole heads of the workload until ~budget_s."""
     import numpy as np
     import oracle
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_threads = max([i.get("num_threads", 1) for i in blas] or [1])
     except Exception:  # pragma: no cover - informational only
         blas_threads = len(os.sched_getaffinity(0))
     B, H = inp.q.shape[0], inp.q.shape[2]
@@ -263,6 +335,10 @@ def cpu_baseline(inp, w, budget_s: float):
         "sample": f"{done} of {len(heads)} (batch, head) pairs of {w.name}, fp64 forward + backward "
                   f"(oracle materialises the full N x N scores), {dt:.1f} s wall",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "os_cpu_count": os.cpu_count(),
+        "blas": [{"vendor": i.get("internal_api"), "version": i.get("version"),
+                  "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
+                 for i in blas],
     }
 
 
@@ -277,6 +353,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (not varlen)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit forward measurement")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (MFMA loop, exponential and FMA rates, copy)")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-attention comparison (materialised N x N scores)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -374,6 +452,13 @@ def main(argv=None) -> int:
     step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(a.steps)) / a.steps
     log("bench: per-kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in per.items()}))
 
+    def pass_summary(name, flops, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        frac = tf / PEAK_BF16_TFLOPS
+        return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_of_peak": round(frac, 4),
+                "target_frac": TARGET_FRAC[name], "target_met": bool(frac >= TARGET_FRAC[name]),
+                "target_ms": round(flops / (TARGET_FRAC[name] * PEAK_BF16_TFLOPS * 1e12) * 1e3, 4)}
+
     unit = gemm_unit(B, H, N, d, w.causal, inp.lengths)
     fwd_fl, bwd_fl = 2 * unit, 5 * unit
     algo = {"fwd": 2 * unit, "bwd_preprocess": 0.0, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
@@ -402,10 +487,8 @@ def main(argv=None) -> int:
             "global_batch": B, "parallelism": "single GPU",
         },
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"ms": round(per["fwd"], 4), "tflops": round(fwd_fl / (per["fwd"] * 1e-3) / 1e12, 2),
-                "frac_of_peak": round(fwd_fl / (per["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 2),
-                "frac_of_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "fwd": pass_summary("fwd", fwd_fl, per["fwd"]),
+        "bwd": pass_summary("bwd", bwd_fl, bwd_ms),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in per.items()},
         "roofline": {
             "kernel": dom,
@@ -442,12 +525,23 @@ def main(argv=None) -> int:
         }
         del o_std
         torch.cuda.empty_cache()
+    if not a.no_ceilings:
+        log("bench: measured ceilings")
+        c = ceilings()
+        out["ceilings"] = c
+        out["roofline"]["peak_from_device_clock"] = c["peak_bf16_tflops_from_clock"]
+        out["roofline"]["peak_measured_mfma_loop"] = c["mfma_bf16_loop_tflops"]
+        out["roofline"]["frac_of_measured"] = round(achieved / c["mfma_bf16_loop_tflops"], 4)
+        # The softmax's exponentials against the measured v_exp_f32 rate: one per visible
+        # score in the forward (B H N^2 / 2 under causal), a lower bound on its time.
+        n_exp = unit / (2.0 * d)
+        out["ceilings"]["fwd_exp_bound_ms"] = round(n_exp / (c["exp_gops"] * 1e9) * 1e3, 4)
     if not a.no_decode:
         log("bench: decode workloads")
         out["decode"] = decode_bench()
     if not a.no_fp8:
         log("bench: 8-bit forward")
-        out["fp8_forward"] = fp8_bench()
+        out["fp8_forward"] = fp8_bench(batch=a.batch, seqlen=a.seqlen)
     if a.cpu_budget > 0 and w.varlen is False:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)

@@ -23,7 +23,7 @@ __all__ = [
     "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
-    "fa_fwd_fp8", "forward_fp8",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_copy",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
@@ -74,6 +74,15 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_decode_workspace_bytes.restype = sz
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_device_info.argtypes = [i32, ip, ip, ip, ctypes.c_char_p, i32]
+    lib.fa_device_info.restype = i32
+    lib.fa_ubench_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    lib.fa_ubench_mfma_bf16.restype = i32
+    lib.fa_ubench_valu.argtypes = [vp, i32, i32, i32, vp]
+    lib.fa_ubench_valu.restype = i32
+    lib.fa_ubench_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.fa_ubench_copy.restype = i32
     _LIB = lib
     return lib
 
@@ -149,6 +158,32 @@ def fa_strerror(status: int) -> str:
     return load_library().fa_strerror(status).decode()
 
 
+# ---------------------------------------------------------------- measurement calls (fa_ubench.h)
+
+def fa_device_info(device: int = 0) -> dict:
+    """Compute units, maximum engine clock (kHz), L2 bytes and architecture name of a device,
+    as the HIP runtime reports them."""
+    cu, clk, l2 = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    arch = ctypes.create_string_buffer(64)
+    st = load_library().fa_device_info(device, ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(l2), arch, 64)
+    if st != FA_OK:
+        raise FAError(st, "fa_device_info")
+    return {"compute_units": cu.value, "max_clock_khz": clk.value, "l2_bytes": l2.value,
+            "arch": arch.value.decode()}
+
+
+def fa_ubench_mfma_bf16(out: int, blocks: int, iters: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_mfma_bf16(out, blocks, iters, stream)
+
+
+def fa_ubench_valu(out: int, blocks: int, iters: int, op: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_valu(out, blocks, iters, op, stream)
+
+
+def fa_ubench_copy(src: int, dst: int, nbytes: int, blocks: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_copy(src, dst, nbytes, blocks, stream)
+
+
 # ---------------------------------------------------------------- torch marshalling
 
 def _dtype_code(t) -> int:
@@ -196,9 +231,28 @@ def _lse_shape(B, H, N, T, varlen: bool):
     return (H, T) if varlen else (B, H, N)
 
 
-def _check_cu(cu_seqlens, B: int) -> None:
+def _check_cu(cu_seqlens, B: int, T: int, max_seqlen: int, validate: bool) -> None:
+    """cu_seqlens must be int32 [B + 1]. With ``validate`` its values are read back to the
+    host (a synchronising copy) and checked, since the kernels trust them: cu[0] = 0,
+    non-decreasing, cu[B] = the packed token count, no sequence longer than max_seqlen.
+    A larger last entry would send the kernels past the ends of the tensors, a longer
+    sequence would leave rows unwritten."""
     import torch
     _expect("cu_seqlens", cu_seqlens, (B + 1,), torch.int32)
+    if int(max_seqlen) < 1:
+        raise ValueError(f"max_seqlen must be >= 1, got {max_seqlen}")
+    if not validate:
+        return
+    cu = [int(c) for c in cu_seqlens.detach().to("cpu").tolist()]
+    if cu[0] != 0:
+        raise ValueError(f"cu_seqlens[0] must be 0, got {cu[0]}")
+    if cu[-1] != T:
+        raise ValueError(f"cu_seqlens[-1] must equal the packed token count {T}, got {cu[-1]}")
+    lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+    if min(lens, default=0) < 0:
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if max(lens, default=0) > int(max_seqlen):
+        raise ValueError(f"a sequence of {max(lens)} tokens is longer than max_seqlen = {max_seqlen}")
 
 
 def _workspace_bytes(t) -> int:
@@ -211,8 +265,10 @@ def _stream(stream):
 
 
 def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, cu_seqlens=None,
-            max_seqlen: Optional[int] = None, out=None, lse=None, stream=None) -> Tuple:
-    """O and the fp32 natural-log LSE of exact attention (see include/fa.h)."""
+            max_seqlen: Optional[int] = None, out=None, lse=None, stream=None, check_cu: bool = True) -> Tuple:
+    """O and the fp32 natural-log LSE of exact attention (see include/fa.h). For a packed
+    batch, ``check_cu`` (default) validates cu_seqlens on a host copy first; pass False to
+    skip that synchronising read when the offsets are known to be well formed."""
     import torch
     B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
     varlen = cu_seqlens is not None
@@ -223,7 +279,7 @@ def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None
     if lse is not None:
         _expect("lse", lse, _lse_shape(B, H, N, T, varlen), torch.float32)
     if varlen:
-        _check_cu(cu_seqlens, B)
+        _check_cu(cu_seqlens, B, T, N, check_cu)
     _check(q, k, v, *(t for t in (out, lse, cu_seqlens) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
@@ -240,8 +296,9 @@ def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
              cu_seqlens=None, max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None) -> Tuple:
-    """(dQ, dK, dV) for the upstream gradient ``dout`` (see include/fa.h)."""
+             workspace=None, stream=None, check_cu: bool = True) -> Tuple:
+    """(dQ, dK, dV) for the upstream gradient ``dout`` (see include/fa.h); ``check_cu`` as
+    in ``forward``."""
     import torch
     B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
     varlen = cu_seqlens is not None
@@ -250,7 +307,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
             _expect(name, t, q.shape, q.dtype)
     _expect("lse", lse, _lse_shape(B, H, N, T, varlen), torch.float32)
     if varlen:
-        _check_cu(cu_seqlens, B)
+        _check_cu(cu_seqlens, B, T, N, check_cu)
     _check(q, k, v, o, lse, dout, *(t for t in (dq, dk, dv, workspace, cu_seqlens) if t is not None))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq

@@ -12,11 +12,16 @@ constexpr size_t kAlign = 16;
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
+// The kernels track the running maximum of the raw scores q.k and exponentiate
+// c * (s - m) with c = scale * log2(e): that is the maximum of the scaled scores only when
+// c > 0, so the scale must be positive (and finite).
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
+
 // Common checks of fa_fwd and fa_bwd; fills the sizes of `pr`.
 int check_common(int batch, int heads, int seqlen, int head_dim, float scale, int causal,
                  const int32_t* cu_seqlens, int total_tokens, int dtype, fa::Problem& pr) {
   if (batch < 1 || heads < 1 || seqlen < 1) return FA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
@@ -53,7 +58,6 @@ int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batc
               int head_dim, float scale, int causal, const int32_t* cu_seqlens, int total_tokens, int dtype) {
   const int st = check_common(batch, heads, seqlen, head_dim, scale, causal, cu_seqlens, total_tokens, dtype, pr);
   if (st != FA_OK) return st;
-  if (scale == 0.f) return FA_ERR_INVALID_ARG;
   const size_t need = workspace_bytes_for(heads, pr.total_tokens);
   if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FA_ERR_WORKSPACE;
@@ -69,7 +73,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 int check_decode(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
                  int num_splits, int dtype, fa::DecodeProblem& pr, size_t* need) {
   if (batch < 1 || heads < 1 || seqlen_q < 1 || seqlen_k < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (causal && seqlen_q > seqlen_k) return FA_ERR_INVALID_ARG;
   if (seqlen_q > fa::kDecodeMaxQ) return FA_ERR_UNSUPPORTED;
@@ -127,7 +131,9 @@ FA_EXPORT int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
                          float descale_v, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(lse)) return FA_ERR_INVALID_ARG;
-  if (!isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v)) return FA_ERR_INVALID_ARG;
+  // The 8-bit kernel's scores are scaled by scale * descale_q * descale_k (see scale_ok).
+  if (!isfinite(descale_v) || !scale_ok(descale_q) || !scale_ok(descale_k)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(softmax_scale * descale_q * descale_k)) return FA_ERR_INVALID_ARG;
   fa::Problem chk{};
   const int st = check_common(batch, heads, seqlen, head_dim, softmax_scale, causal, nullptr, 0, FA_DTYPE_BF16,
                               chk);

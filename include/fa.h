@@ -38,6 +38,11 @@
  *  - head_dim in {64, 128}; seqlen >= 1; batch >= 1; heads >= 1; every tensor pointer
  *    16-byte aligned. Queries and keys share one length (self-attention).
  *  - causal != 0: query i sees key j iff j <= i, within its own sequence.
+ *  - softmax_scale must be finite and > 0 (every entry point returns
+ *    FA_ERR_INVALID_ARG otherwise): the kernels keep the running maximum of the raw
+ *    scores q.k, which is the maximum of the scaled scores only for a positive scale.
+ *  - stream is a hipStream_t passed as void* (the same pointer value), so that this
+ *    header compiles without the HIP headers.
  *  - Argument checks run on the host before any HIP call and return
  *    FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_WORKSPACE without touching the
  *    device. A failed launch returns FA_ERR_HIP.
@@ -81,6 +86,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int dtype, void* stream);
 
 /*
+ * (A reading: the pages fix what the backward computes, not how a library hands it
+ * scratch memory; a caller-owned workspace keeps the library free of allocations.)
  * Bytes of device workspace fa_bwd needs: two fp32 row statistics per (head, query
  * row), D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale, each array rounded up to
  * 256 bytes. For a packed batch (varlen != 0) pass total_tokens; otherwise it is
@@ -101,7 +108,6 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
  *   3. the dQ accumulation pass: one workgroup per (sequence, head, query tile)
  *      accumulating dQ on chip while it walks the key tiles.
  * No atomics: the result is bitwise deterministic from run to run.
- * softmax_scale must be finite and nonzero (the backward works with LSE / scale).
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller; its contents on entry do not matter.
  */
@@ -187,14 +193,18 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
  * probabilities are rounded to E4M3 (round to nearest even, relative error <= 2^-4)
  * before P V; the row sums use the unrounded fp32 P. O therefore differs from the exact
  * attention of the real inputs by about 2^-4 / sqrt(3) of its size in relative L2 (the
- * tests allow 5e-2). Padded batches only (no cu_seqlens). All pointers 16-byte aligned.
+ * tests allow 5e-2). Padded batches only (no cu_seqlens). All pointers 16-byte aligned. descale_q and
+ * descale_k must be finite and > 0, and so must softmax_scale * descale_q * descale_k
+ * (the scale the kernel applies to the raw 8-bit scores); descale_v must be finite.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int batch, int heads, int seqlen, int head_dim,
                float softmax_scale, float descale_q, float descale_k, float descale_v,
                int causal, void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL). Not from the pages
+ * (whose interface is a switch in a training library): the ABI reports errors as status
+ * codes instead of exceptions, and this names them. */
 const char* fa_strerror(int status);
 
 #ifdef __cplusplus

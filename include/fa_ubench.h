@@ -1,0 +1,51 @@
+/*
+ * fa_ubench.h - device facts and measured ceilings for the roofline of libfa's kernels
+ * (part of libfa.so; not part of the attention path itself).
+ *
+ * The attention kernels are bounded by the matrix cores (the pages' point that GEMM
+ * units do most of the FLOPs: "FlashAttention-2 (PT)", "1. Minimização de operações não
+ * matriciais"), with the vector ALUs' exponentials and the HBM bandwidth as secondary
+ * ceilings ("Pensar en la E/S" in the AI Atlas summary). These calls report the device's
+ * compute-unit count and clock, from which the dense MFMA peak follows, and run loops
+ * that measure what the chip sustains for each ceiling.
+ *
+ * Conventions: pointers are device pointers owned by the caller; work is enqueued on
+ * `stream` (a hipStream_t passed as void*) and timed by the caller around the call.
+ * Return FA_UB_OK, FA_UB_ERR_INVALID_ARG (checked on the host before any launch) or
+ * FA_UB_ERR_HIP (a HIP call or launch failed).
+ */
+#ifndef FA_UBENCH_H_
+#define FA_UBENCH_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { FA_UB_OK = 0, FA_UB_ERR_INVALID_ARG = 1, FA_UB_ERR_HIP = 4 };
+
+/* Compute units, maximum engine clock (kHz) and L2 size (bytes) of `device` as the HIP
+ * runtime reports them, and its architecture name (NUL-terminated, truncated to
+ * arch_len - 1 characters; arch may be NULL when arch_len is 0). Host pointers. */
+int fa_device_info(int device, int* compute_units, int* max_clock_khz, int* l2_bytes, char* arch,
+                   int arch_len);
+
+/* `blocks` workgroups of four waves; each wave issues 4 * iters independent
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each). out: blocks * 256 floats (written). */
+int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* stream);
+
+/* `blocks` workgroups of 256 lanes; each lane runs 8 * iters vector operations in eight
+ * independent chains: op 0 the exponential v_exp_f32, op 1 an fp32 FMA (2 FLOP).
+ * out: blocks * 256 floats (written). */
+int fa_ubench_valu(float* out, int blocks, int iters, int op, void* stream);
+
+/* Copies `bytes` (a multiple of 16; src and dst 16-byte aligned, not overlapping) from
+ * src to dst with `blocks` workgroups of 256 lanes, 16 bytes per lane per access. */
+int fa_ubench_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_UBENCH_H_ */

@@ -12,6 +12,8 @@ import exact_io_aware_attention_amd as fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 A = 1 << 20          # a 16-byte-aligned fake device address: never dereferenced on these paths
 MIS = A + 2          # misaligned
@@ -23,10 +25,12 @@ def _lib():
     return fa.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+def declared_functions(headers=(HEADER,)):
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -35,12 +39,18 @@ def test_header_declares_the_boundary():
                                     "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_strerror"]
 
 
+def test_measurement_header_declares_its_calls():
+    assert declared_functions([os.path.join(ROOT, "include", "fa_ubench.h")]) == [
+        "fa_device_info", "fa_ubench_copy", "fa_ubench_mfma_bf16", "fa_ubench_valu"]
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
-    for name in declared_functions():
+    assert len(HEADERS) >= 2
+    for name in declared_functions(HEADERS):
         assert name in exported, name
         assert getattr(lib, name) is not None
 
@@ -79,6 +89,9 @@ def _bwd(**kw):
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
     (dict(softmax_scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),    # the scale must be positive
+    (dict(softmax_scale=-0.125), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.0), fa.FA_ERR_INVALID_ARG),
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
     (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
@@ -97,7 +110,8 @@ def test_fwd_argument_checks(kw, code):
     (dict(dv=MIS), fa.FA_ERR_INVALID_ARG),
     (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
     (dict(workspace=None), fa.FA_ERR_WORKSPACE),
-    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),   # the backward works with LSE / scale
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),   # the scale must be positive
+    (dict(softmax_scale=-1.0), fa.FA_ERR_INVALID_ARG),
     (dict(workspace_bytes=255), fa.FA_ERR_WORKSPACE),
     (dict(workspace=A + 16), fa.FA_ERR_WORKSPACE),
     (dict(seqlen=-5), fa.FA_ERR_INVALID_ARG),
@@ -120,6 +134,11 @@ def test_stage_argument_checks():
     assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, workspace=None, workspace_bytes=0, **pre,
                                 **common) == fa.FA_ERR_WORKSPACE
     assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, **ws, softmax_scale=0.0, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, **ws, softmax_scale=-0.5, **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=A, dv=A, **ws, softmax_scale=-0.1, causal=0,
+                          **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dq(q=A, k=A, v=A, dout=A, lse=A, dq=A, **ws, softmax_scale=0.0, causal=0,
+                        **common) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_preprocess(o=A, dout=A, lse=A, **ws, **pre, **dict(common, head_dim=48)) == fa.FA_ERR_UNSUPPORTED
     sc = dict(softmax_scale=0.125, causal=1)
     assert fa.fa_bwd_dkdv(q=A, k=A, v=A, dout=A, lse=A, dk=None, dv=A, **ws, **sc, **common) == fa.FA_ERR_INVALID_ARG
@@ -181,6 +200,8 @@ def _dec(**kw):
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.1), fa.FA_ERR_INVALID_ARG),
     (dict(), fa.FA_ERR_WORKSPACE),                                   # no workspace
     (dict(workspace=A, workspace_bytes=16), fa.FA_ERR_WORKSPACE),    # too small
     (dict(workspace=A + 16, workspace_bytes=1 << 30), fa.FA_ERR_WORKSPACE),  # not 256-aligned
@@ -225,9 +246,27 @@ def _fp8(**kw):
     (dict(softmax_scale=math.nan), fa.FA_ERR_INVALID_ARG),
     (dict(descale_q=math.inf), fa.FA_ERR_INVALID_ARG),
     (dict(descale_v=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_q=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_k=-2.0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_q=1e-30, descale_k=1e-30), fa.FA_ERR_INVALID_ARG),  # the product underflows to 0
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fp8_argument_checks(kw, code):
     _lib()
     assert _fp8(**kw) == code
 
+
+
+# ---------------------------------------------------------------- measurement calls
+
+def test_ubench_argument_checks():
+    _lib()
+    assert fa.fa_ubench_mfma_bf16(None, 1, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_bf16(A, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_valu(A, 1, 0, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_valu(A, 1, 1, 2, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_copy(A, A + 4096, 100, 8, None) == fa.FA_ERR_INVALID_ARG   # not a multiple of 16
+    assert fa.fa_ubench_copy(A + 8, A + 4096, 256, 8, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_copy(A, A + 4096, 256, 0, None) == fa.FA_ERR_INVALID_ARG

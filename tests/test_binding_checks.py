@@ -78,3 +78,39 @@ def test_matching_host_tensors_stop_at_the_device_check():
     q = t(B, N, H, D)
     with pytest.raises(ValueError, match="contiguous device tensors"):
         fa.forward(q, t(B, N, H, D), t(B, N, H, D))
+
+
+@pytest.mark.parametrize("cu,max_seqlen,msg", [
+    ([1, 40, 100], 60, "cu_seqlens\\[0\\] must be 0"),
+    ([0, 40, 120], 80, "must equal the packed token count 100"),     # would run past the tensors
+    ([0, 40, 90], 60, "must equal the packed token count 100"),
+    ([0, 70, 100], 60, "longer than max_seqlen = 60"),              # would leave rows unwritten
+    ([0, 60, 50, 100], 60, "non-decreasing"),
+])
+def test_packed_offsets_are_validated(cu, max_seqlen, msg):
+    T = 100
+    q = t(T, H, D)
+    cu_t = torch.tensor(cu, dtype=torch.int32)
+    with pytest.raises(ValueError, match=msg):
+        fa.forward(q, t(T, H, D), t(T, H, D), cu_seqlens=cu_t, max_seqlen=max_seqlen)
+    nseq = len(cu) - 1
+    lse = t(H, T, dtype=torch.float32)
+    with pytest.raises(ValueError, match=msg):
+        fa.backward(q, t(T, H, D), t(T, H, D), t(T, H, D), lse, t(T, H, D), cu_seqlens=cu_t,
+                    max_seqlen=max_seqlen)
+    assert nseq >= 2
+
+
+def test_packed_offsets_check_can_be_skipped_and_max_seqlen_must_be_positive():
+    T = 100
+    q = t(T, H, D)
+    bad = torch.tensor([0, 70, 100], dtype=torch.int32)
+    # without the check the call gets as far as the device test (host tensors here)
+    with pytest.raises(ValueError, match="contiguous device tensors"):
+        fa.forward(q, t(T, H, D), t(T, H, D), cu_seqlens=bad, max_seqlen=60, check_cu=False)
+    with pytest.raises(ValueError, match="max_seqlen must be >= 1"):
+        fa.forward(q, t(T, H, D), t(T, H, D), cu_seqlens=torch.tensor([0, 100], dtype=torch.int32),
+                   max_seqlen=0)
+    good = torch.tensor([0, 40, 100], dtype=torch.int32)
+    with pytest.raises(ValueError, match="contiguous device tensors"):
+        fa.forward(q, t(T, H, D), t(T, H, D), cu_seqlens=good, max_seqlen=60)

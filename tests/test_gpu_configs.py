@@ -4,14 +4,20 @@ checked against the oracle on outputs it can compute one by one:
 * c1 (1x1x128, d=64, fp32): every output.
 * c2 (8x16x2048, d=64) and c3 (4x32x4096, d=128, causal): whole heads sampled from
   the batch (each head is independent of the others).
-* c4 (1x8x65536, d=64): O, LSE and dQ on 256 seeded query rows of every head; dK and
-  dV need every query row's softmax, which costs the oracle minutes per head, so at
-  full size they are held to gradient identities that hold at any size, and their
-  exact parity is checked at the same settings with N = 8192. Memory: the library
-  allocates nothing and its workspace is O(N).
+* c4 (1x8x65536, d=64): O, LSE and dQ on 256 seeded query rows of every head, and dK
+  and dV on 256 seeded key rows of every head. A key row's gradients sum over every
+  query row's softmax, which costs the oracle about a minute per head, so those
+  expected values were computed once by tests/golden/make_c4_key_rows.py (the oracle
+  alone, on the same seeded inputs, whose digests the file records) and are read from
+  tests/golden/c4_key_rows.npz. Gradient identities that hold at any size cover every
+  row, and exact parity of whole heads runs at the same settings with N = 8192. Memory:
+  the library allocates nothing and its workspace is O(N).
 * c5 (16384 packed tokens, causal per sequence): sampled sequences x heads, including
   the truncated last sequence.
 """
+import hashlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +27,8 @@ import workloads as W
 from parity_utils import check, f64, run_gpu
 
 pytestmark = pytest.mark.gpu
+
+GOLDEN_C4 = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "c4_key_rows.npz")
 
 
 def _head(t, b, h):
@@ -109,6 +117,16 @@ def test_c4_full_size():
         assert abs(tq - tk) <= 3e-2 * max(abs(tq), np.sqrt(n) * np.sqrt((dqh ** 2).mean())), (h, tq, tk)
         print(f"c4 h{h} identities: |sum dV - sum dO| {err_v:.3e} |sum dK| {err_k:.3e} "
               f"tr(Q'dQ) {tq:.4e} tr(K'dK) {tk:.4e}", flush=True)
+    # dK and dV, element by element, on 256 seeded key rows of every head.
+    gold = np.load(GOLDEN_C4)
+    digests = [hashlib.sha256(t.contiguous().view(-1).view(torch.uint8).numpy().tobytes()).hexdigest()
+               for t in (inp.q, inp.k, inp.v, inp.do)]
+    assert list(gold["sha256"]) == digests, "c4 inputs differ from those the stored key rows were computed on"
+    keys = gold["keys"]
+    assert np.array_equal(keys, W.sample_rows(w.seed + 100, w.seqlen, 256))
+    for h in range(w.heads):
+        check(f"c4 h{h} dK[256 key rows]", "bf16", dk[0, keys, h, :], gold["dk"][h].astype(np.float64), "g")
+        check(f"c4 h{h} dV[256 key rows]", "bf16", dv[0, keys, h, :], gold["dv"][h].astype(np.float64), "g")
 
 
 def test_c4_library_allocates_nothing():
