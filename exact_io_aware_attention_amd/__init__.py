@@ -3,8 +3,8 @@
 A thin Python binding over ``libfa.so``, whose C ABI is declared in ``include/fa.h``.
 The raw entry points keep the C names and take integer device pointers:
 
-    fa_fwd, fa_bwd, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_workspace_bytes,
-    fa_fwd_decode, fa_fwd_decode_workspace_bytes, fa_fwd_fp8, fa_strerror
+    fa_fwd, fa_bwd, fa_bwd_noalloc, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq,
+    fa_bwd_workspace_bytes, fa_fwd_decode, fa_fwd_decode_workspace_bytes, fa_fwd_fp8, fa_strerror
 
 ``forward``, ``backward``, ``decode`` and ``forward_fp8`` marshal torch tensors (device memory and the current
 stream) into those calls; every step of the computation runs in the HIP kernels.
@@ -19,14 +19,16 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_SCRATCH",
+    "FA_BWD_NOALLOC_MAX_SCRATCH", "fa_bwd_noalloc",
     "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
     "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_copy",
 ]
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+FA_BWD_NOALLOC_MAX_SCRATCH = 16 << 20   # bytes of fa_bwd_noalloc's fixed device array (include/fa.h)
 FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +60,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32,
+                                   vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i32, i32, i32, i32, f32, vp, i32, i32, vp]
     lib.fa_bwd_preprocess.restype = i32
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
@@ -103,6 +108,13 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
                                  batch, heads, seqlen, head_dim, softmax_scale, int(causal),
                                  cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, batch: int,
+                   heads: int, seqlen: int, head_dim: int, softmax_scale: float, causal: int,
+                   cu_seqlens: Optional[int], total_tokens: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, seqlen, head_dim,
+                                         softmax_scale, int(causal), cu_seqlens, total_tokens, dtype, stream)
 
 
 def fa_bwd_preprocess(o: int, dout: int, lse: int, workspace: int, workspace_bytes: int, batch: int, heads: int,

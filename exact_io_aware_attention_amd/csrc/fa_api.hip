@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_launch.h"
 
@@ -98,6 +100,40 @@ int check_decode(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
   pr.scale = scale;
   pr.causal = causal != 0;
   return FA_OK;
+}
+
+// Scratch memory of fa_bwd_noalloc: the backward's row statistics (D and -LSE / scale)
+// in a fixed device array, for callers that cannot allocate. Each GPU the library runs
+// on holds its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is used.
+constexpr size_t kScratchBytes = FA_BWD_NOALLOC_MAX_SCRATCH;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or nullptr with *err set.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || ptr == nullptr) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -250,6 +286,30 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
                    softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
 }
 
+FA_EXPORT int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int seqlen,
+                             int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,
+                             int total_tokens, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(dout) || !aligned(lse) ||
+      !aligned(dq) || !aligned(dk) || !aligned(dv))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem chk{};
+  const int st = check_common(batch, heads, seqlen, head_dim, softmax_scale, causal, cu_seqlens, total_tokens,
+                              dtype, chk);
+  if (st != FA_OK) return st;
+  const size_t need = workspace_bytes_for(heads, chk.total_tokens);
+  if (need > kScratchBytes) return FA_ERR_SCRATCH;
+  if (chk.total_tokens == 0) return FA_OK;
+  hipError_t err = hipSuccess;
+  void* ws = scratch_on_current_device(&err);
+  if (ws == nullptr) return FA_ERR_HIP;
+  // The same three kernels as fa_bwd, with the scratch array as the workspace. Nothing in
+  // it needs clearing: the preprocess writes every statistic the later kernels read.
+  return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, kScratchBytes, batch, heads, seqlen, head_dim,
+                softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+}
+
 FA_EXPORT size_t fa_fwd_decode_workspace_bytes(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
                                                int num_splits) {
   fa::DecodeProblem pr{};
@@ -290,6 +350,9 @@ FA_EXPORT const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype (head_dim 64 or 128; bf16 or fp32)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_HIP: return "HIP kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "problem needs more scratch than fa_bwd_noalloc's fixed device array holds "
+             "(8 * heads * tokens bytes > FA_BWD_NOALLOC_MAX_SCRATCH); use fa_bwd with a workspace";
     default: return "unknown status code";
   }
 }

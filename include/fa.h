@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad alignment, overflow */
   FA_ERR_UNSUPPORTED = 2,  /* head_dim or dtype outside what the kernels are built for */
   FA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than required        */
-  FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError != success)      */
+  FA_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError != success)      */
+  FA_ERR_SCRATCH = 5       /* fa_bwd_noalloc: problem larger than its fixed scratch     */
 } fa_status;
 
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
@@ -119,6 +120,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float softmax_scale, int causal,
            const int32_t* cu_seqlens, int total_tokens,
            int dtype, void* stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results. The row statistics go to a fixed device array
+ * inside the library instead, FA_BWD_NOALLOC_MAX_SCRATCH bytes per GPU, held from the
+ * library's first use on that GPU until the process ends; problems needing more than that
+ * (8 * heads * tokens bytes, tokens = batch * seqlen or total_tokens: up to 2^21
+ * (head, token) pairs, e.g. 32 heads x 65536 tokens) return FA_ERR_SCRATCH without
+ * launching. No call allocates (no hipMalloc, no allocating library routine); the first
+ * call on a device looks up the array's device address once (hipGetSymbolAddress), on
+ * the calling thread's current device, which must be the device of the tensors and the
+ * stream. Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and give wrong results; calls in stream order
+ * are safe.
+ */
+#define FA_BWD_NOALLOC_MAX_SCRATCH (16u << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv,
+                   int batch, int heads, int seqlen, int head_dim,
+                   float softmax_scale, int causal,
+                   const int32_t* cu_seqlens, int total_tokens,
+                   int dtype, void* stream);
 
 /*
  * The three stages of fa_bwd, callable on their own (same arguments, conventions and

@@ -34,7 +34,7 @@ def declared_functions(headers=(HEADER,)):
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_noalloc", "fa_bwd_preprocess",
                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
                                     "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_strerror"]
 
@@ -162,7 +162,7 @@ def test_workspace_size():
 def test_strerror_covers_every_code():
     _lib()
     seen = set()
-    for code in range(5):
+    for code in range(6):
         s = fa.fa_strerror(code)
         assert s and s not in seen
         seen.add(s)
@@ -270,3 +270,30 @@ def test_ubench_argument_checks():
     assert fa.fa_ubench_copy(A, A + 4096, 100, 8, None) == fa.FA_ERR_INVALID_ARG   # not a multiple of 16
     assert fa.fa_ubench_copy(A + 8, A + 4096, 256, 8, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_copy(A, A + 4096, 256, 0, None) == fa.FA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- backward without allocation
+
+def _noalloc(**kw):
+    args = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, batch=1, heads=1, seqlen=16, head_dim=64,
+                softmax_scale=0.125, causal=0, cu_seqlens=None, total_tokens=0, dtype=fa.FA_DTYPE_BF16,
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(head_dim=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dv=MIS), fa.FA_ERR_INVALID_ARG),
+    # 8 bytes per (head, token): 2^21 pairs fit the 16 MiB array, one token more does not
+    (dict(batch=1, heads=32, seqlen=65537), fa.FA_ERR_SCRATCH),
+    (dict(batch=2, heads=16, seqlen=65536 + 64), fa.FA_ERR_SCRATCH),
+    (dict(cu_seqlens=A, total_tokens=(1 << 21) + 1, seqlen=2048, batch=4), fa.FA_ERR_SCRATCH),
+    (dict(cu_seqlens=A, total_tokens=0), fa.FA_OK),   # empty packed batch: nothing to launch
+])
+def test_noalloc_argument_checks(kw, code):
+    _lib()
+    assert _noalloc(**kw) == code
+    assert fa.FA_BWD_NOALLOC_MAX_SCRATCH == 16 << 20
