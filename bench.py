@@ -278,6 +278,9 @@ def ceilings(reps: int = 5):
     t_mfma = timed(lambda: ok(fa.fa_ubench_mfma_bf16(out.data_ptr(), mblocks, miters, sp), "mfma"))
     t_exp = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 0, sp), "exp"))
     t_fma = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 1, sp), "fma"))
+    lblocks, liters = 4 * cus, 1000          # four waves per SIMD
+    t_ldsr = timed(lambda: ok(fa.fa_ubench_lds(out.data_ptr(), lblocks, liters, 0, sp), "lds rows"))
+    t_ldst = timed(lambda: ok(fa.fa_ubench_lds(out.data_ptr(), lblocks, liters, 1, sp), "lds transposed"))
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
     dst = torch.empty_like(src)
@@ -296,7 +299,14 @@ def ceilings(reps: int = 5):
         "fma_fp32_tflops": round(2 * lane_ops / (t_fma * 1e-3) / 1e12, 1),
         "fma_lane_ops_per_clk_cu": round(lane_ops / (t_fma * 1e-3) / clk_hz / cus, 2),
         "copy_gbs": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
-        "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4)},
+        # LDS operand reads per clock per CU (wave instructions): what bounds an MFMA whose
+        # operand comes from LDS (one row read, or two transpose reads, per MFMA)
+        "lds_b128_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldsr * 1e-3) / clk_hz / cus, 4),
+        "lds_tr16_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldst * 1e-3) / clk_hz / cus, 4),
+        "lds_b128_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldsr * 1e-3) / 1e12, 1),
+        "lds_tr16_tbs": round(lblocks * 4 * liters * 8 * 512 / (t_ldst * 1e-3) / 1e12, 1),
+        "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
+               "lds_rows": round(t_ldsr, 4), "lds_tr": round(t_ldst, 4)},
         "note": "rates per clock use the reported maximum clock; the clock under load may be lower",
     }
 
@@ -358,8 +368,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-attention comparison (materialised N x N scores)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="before the warmup, run a plain fp32 copy kernel (y = -x) over this many MiB, "
-                         "three times, as the known-size reference for HBM byte counters")
+                    help="before the warmup, run the library's copy kernel over this many MiB, three times, "
+                         "as the known-size reference for the byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): every (sequence, head) pair is "
@@ -421,14 +431,17 @@ def main(argv=None) -> int:
 
     kernels = [("fwd", k_fwd), ("bwd_preprocess", k_pre), ("bwd_dkdv", k_dkdv), ("bwd_dq", k_dq)]
     if a.calibrate_copy_mib > 0:
-        n = a.calibrate_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, device=dev, dtype=torch.float32)
+        # The library's copy kernel (16-byte loads and stores per lane, like the kernels'
+        # tile copies): it reads and writes calibrate_copy_mib MiB per launch, the known
+        # sizes that the byte counters of the attention kernels are scaled against.
+        nbytes = a.calibrate_copy_mib * (1 << 20)
+        src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.neg(src, out=dst)  # reads and writes calibrate_copy_mib MiB each
+            check(fa.fa_ubench_copy(src.data_ptr(), dst.data_ptr(), nbytes, 4096, sp), "fa_ubench_copy")
         torch.cuda.synchronize()
-        log(f"bench: copy calibration, {a.calibrate_copy_mib} MiB read + {a.calibrate_copy_mib} MiB written "
-            f"per launch, 3 launches")
+        log(f"bench: copy calibration (ub_copy_kernel), {a.calibrate_copy_mib} MiB read + "
+            f"{a.calibrate_copy_mib} MiB written per launch, 3 launches")
         del src, dst
     log(f"bench: warmup {a.warmup}")
     for _ in range(a.warmup):

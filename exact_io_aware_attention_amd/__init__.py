@@ -24,7 +24,7 @@ __all__ = [
     "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
-    "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_copy",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_lds", "fa_ubench_copy",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
@@ -86,6 +86,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_ubench_mfma_bf16.restype = i32
     lib.fa_ubench_valu.argtypes = [vp, i32, i32, i32, vp]
     lib.fa_ubench_valu.restype = i32
+    lib.fa_ubench_lds.argtypes = [vp, i32, i32, i32, vp]
+    lib.fa_ubench_lds.restype = i32
     lib.fa_ubench_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.fa_ubench_copy.restype = i32
     _LIB = lib
@@ -190,6 +192,10 @@ def fa_ubench_mfma_bf16(out: int, blocks: int, iters: int, stream: Optional[int]
 
 def fa_ubench_valu(out: int, blocks: int, iters: int, op: int, stream: Optional[int]) -> int:
     return load_library().fa_ubench_valu(out, blocks, iters, op, stream)
+
+
+def fa_ubench_lds(out: int, blocks: int, iters: int, op: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_lds(out, blocks, iters, op, stream)
 
 
 def fa_ubench_copy(src: int, dst: int, nbytes: int, blocks: int, stream: Optional[int]) -> int:

@@ -934,7 +934,7 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
 
 // One query tile of one (sequence, head) of the dQ pass. The two LDS buffers are free
 // again when it returns (its last step ends in a barrier).
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool DESC = false>
 __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
                                          u16* buf1) {
 #if __HIP_DEVICE_COMPILE__
@@ -973,12 +973,16 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
   static_assert(L::KP == L::VP, "K and V tiles share their copy offsets");
   TileDma<BC, D, L::KP, kDqWaves, true> kvdma;
   kvdma.init(stride, w, lane);
-  auto issue = [&](int kt, u16* buf) {
+  // Step i visits key tile i, or with DESC tile n_kt - 1 - i (the sum over key tiles
+  // does not depend on their order).
+  auto tile_at = [&](int i) { return DESC ? n_kt - 1 - i : i; };
+  auto issue = [&](int i, u16* buf) {
+    const int kt = tile_at(i);
     kvdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
     kvdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
   };
-  auto compute = [&](int kt, const u16* buf) {
-    const int k0 = kt * BC;
+  auto compute = [&](int i, const u16* buf) {
+    const int k0 = tile_at(i) * BC;
     if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
       const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);
       dq_tile<D, CAUSAL>(st, buf, k0, len, qi, lane, p.c, mask);
@@ -1019,7 +1023,9 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
 // Two workgroups per compute unit (two waves per SIMD) keep the matrix pipe busy while
 // the other wave waits on LDS or does its softmax arithmetic. Workgroup -> (sequence,
 // head, slot) as in the forward: head-grouped per XCD; under causal masking slot i takes
-// query tiles nt-1-i and i, so every workgroup visits the same number of key tiles.
+// query tiles nt-1-i and i, so every workgroup visits the same number of key tiles, the
+// second tile's keys in descending order (co-resident workgroups then read the same key
+// tile at the same step; see the forward kernel).
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
   using L = DqLds<D>;
@@ -1042,7 +1048,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
     const int t_hi = nt - 1 - slot;
     if (t_hi < slot) return;
     dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, t_hi, buf0, buf1);
-    if (slot < t_hi) dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);
+    if (slot < t_hi) dq_qtile<D, CAUSAL, VARLEN, true>(p, b, h, start, len, slot, buf0, buf1);
   } else {
     if (slot >= nt) return;
     dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);

@@ -481,7 +481,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
 
 // One query tile of one (sequence, head): the key loop and the epilogue. The two LDS
 // buffers are free again when it returns (its last step ends in a barrier).
-template <int D, bool CAUSAL, bool VARLEN, int QB>
+template <int D, bool CAUSAL, bool VARLEN, int QB, bool DESC = false>
 __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
                                           u16* buf1) {
 #if __HIP_DEVICE_COMPILE__
@@ -524,12 +524,16 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
   TileDma<BC, D, L::VP, NW> vdma;
   kdma.init(stride, w, lane);
   vdma.init(stride, w, lane);
-  auto issue = [&](int kt, u16* buf) {
+  // Step i of the key loop visits key tile i, or with DESC tile n_kt - 1 - i: the
+  // online softmax combines the blocks in any order.
+  auto tile_at = [&](int i) { return DESC ? n_kt - 1 - i : i; };
+  auto issue = [&](int i, u16* buf) {
+    const int kt = tile_at(i);
     kdma.issue(buf, Kg, kt * BC, len, stride, w, lane);
     vdma.issue(buf + L::KSZ, Vg, kt * BC, len, stride, w, lane);
   };
-  auto compute = [&](int kt, const u16* buf) {
-    const int k0 = kt * BC;
+  auto compute = [&](int i, const u16* buf) {
+    const int k0 = tile_at(i) * BC;
     // wave-uniform: skip tiles that are entirely masked for this wave
     if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
       const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);
@@ -619,7 +623,12 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
 // resident on one XCD share few heads and stream the same K/V rows through its L2 (this
 // keeps the fabric traffic near the O(N d) operand bytes at long sequences). Without
 // masking a slot is one query tile; under causal masking tile t visits t + 1 key tiles,
-// so slot i takes tiles nt-1-i and i and every workgroup does the same work.
+// so slot i takes tiles nt-1-i and i and every workgroup does the same work. The first
+// tile walks the keys upwards from 0, the second downwards from its diagonal: workgroup
+// i reaches its second tile after nt - i steps and key tile j of it at step nt - j, the
+// same step for every workgroup, so at any moment the co-resident workgroups of a head
+// read two key tiles between them (one in each direction) and the head's K/V passes
+// through L2 about once, however long the sequence.
 template <int D, bool CAUSAL, bool VARLEN, int QB>
 __global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd_bf16_kernel(FwdParams p) {
   constexpr int BR = 32 * QB * fwd_waves<QB>();
@@ -643,7 +652,7 @@ __global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd
     const int t_hi = nt - 1 - slot;
     if (t_hi < slot) return;
     fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, t_hi, buf0, buf1);
-    if (slot < t_hi) fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, slot, buf0, buf1);
+    if (slot < t_hi) fwd_qtile<D, CAUSAL, VARLEN, QB, true>(p, b, h, start, len, slot, buf0, buf1);
   } else {
     if (slot >= nt) return;
     fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, slot, buf0, buf1);

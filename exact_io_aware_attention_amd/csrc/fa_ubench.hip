@@ -58,6 +58,41 @@ __global__ __launch_bounds__(kUbThreads) void ub_valu_kernel(float* __restrict__
   out[(size_t)blockIdx.x * kUbThreads + tid] = s;
 }
 
+// LDS operand reads as the attention kernels issue them, eight per step in every wave:
+// op 0 row-wise 16-byte reads (ds_read_b128: lane l reads row l % 32, chunk l / 32, of a
+// tile with a 68-dword pitch, conflict-free), op 1 transpose reads (ds_read_b64_tr_b16 in
+// the operand pattern of lds_tr_operand on a tile with an 80-dword pitch). The rows read
+// move by 16 each step so the loads stay in the loop; their bits are folded into `out`.
+constexpr int kUbLdsElems = 32768;  // 64 KiB of bf16
+
+__global__ __launch_bounds__(kUbThreads) void ub_lds_kernel(float* __restrict__ out, int iters, int op) {
+  __shared__ __attribute__((aligned(16))) u16 lds[kUbLdsElems];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < kUbLdsElems; i += kUbThreads) lds[i] = (u16)(i * 2654435761u >> 16);
+  __syncthreads();
+  uint32_t acc = 0;
+  if (op == 0) {
+    constexpr int P = 136;  // pitch_rows<128>()
+    const u16* base = lds + (lane & 31) * P + 8 * (lane >> 5);
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (((i * 8 + j) & 7) * 16) * P + 16 * (j & 3));
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+  } else {
+    constexpr int P = 160;  // pitch_tr<128>()
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 v = lds_tr_operand(lds, P, ((i * 8 + j) & 7) * 16, 32 * (j & 3), lane);
+        const u32x4 u = __builtin_bit_cast(u32x4, v);
+        acc ^= u[0] ^ u[1] ^ u[2] ^ u[3];
+      }
+  }
+  out[(size_t)blockIdx.x * kUbThreads + tid] = __uint_as_float(acc);
+}
+
 // dst = src, 16 bytes per lane per access, grid-stride.
 __global__ __launch_bounds__(kUbThreads) void ub_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                              size_t n) {
@@ -97,6 +132,13 @@ FA_EXPORT int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* strea
 FA_EXPORT int fa_ubench_valu(float* out, int blocks, int iters, int op, void* stream) {
   if (!out || blocks < 1 || iters < 1 || (op != 0 && op != 1)) return FA_UB_ERR_INVALID_ARG;
   hipLaunchKernelGGL(fa::ub_valu_kernel, dim3(blocks), dim3(fa::kUbThreads), 0, static_cast<hipStream_t>(stream),
+                     out, iters, op);
+  return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
+}
+
+FA_EXPORT int fa_ubench_lds(float* out, int blocks, int iters, int op, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || (op != 0 && op != 1)) return FA_UB_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fa::ub_lds_kernel, dim3(blocks), dim3(fa::kUbThreads), 0, static_cast<hipStream_t>(stream),
                      out, iters, op);
   return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
 }

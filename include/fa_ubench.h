@@ -40,6 +40,12 @@ int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* stream);
  * out: blocks * 256 floats (written). */
 int fa_ubench_valu(float* out, int blocks, int iters, int op, void* stream);
 
+/* `blocks` workgroups of four waves, each with a 64 KiB LDS tile; every wave issues
+ * 8 * iters LDS operand reads in the forms the attention kernels use: op 0 row-wise
+ * ds_read_b128 (1 KiB per wave instruction), op 1 transpose reads ds_read_b64_tr_b16
+ * (512 B). Bank-conflict-free addressing. out: blocks * 256 floats (written). */
+int fa_ubench_lds(float* out, int blocks, int iters, int op, void* stream);
+
 /* Copies `bytes` (a multiple of 16; src and dst 16-byte aligned, not overlapping) from
  * src to dst with `blocks` workgroups of 256 lanes, 16 bytes per lane per access. */
 int fa_ubench_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
