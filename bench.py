@@ -3,16 +3,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
-A step is one pass of the whole hot path over one batch: fa_fwd, then the three
-backward kernels (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), on synthetic seeded
-inputs already resident in HBM. The default workload is the Llama-shaped causal case
+A step is one pass of the whole hot path over one batch: fa_fwd, then the backward as
+fa_bwd runs it (fa_bwd_dq_stats: the dQ pass, which also forms the row statistics; then
+fa_bwd_dkdv), on synthetic seeded inputs already resident in HBM. The default workload is the Llama-shaped causal case
 (B=4, H=32, N=4096, d=128, bf16). Prints one JSON line.
 
 FLOP model (algorithmic work, not what the kernels happen to execute): one "GEMM
 unit" is 2*B*H*N^2*d, halved under causal masking. Forward = 2 units (QK^T, PV);
 backward = 5 units (recomputed QK^T, dO V^T, P^T dO, dS^T Q, dS K), i.e. 2.5x the
 forward. Per kernel: fwd 2 units, dkdv 4, dq 1 (its recomputation of S and dP is the
-price of a dQ pass without atomics and is not counted), preprocess 0.
+price of a dQ pass without atomics and is not counted).
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same workload
 (whole heads, forward + backward), on the host cores, and reports the same FLOP
@@ -51,10 +51,6 @@ TRAFFIC = {
                   "fetch_factor": 2.0, "write_factor": 1.0,
                   "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_preprocess"): {"bytes": 274770234, "fetch_kib": 132120.1, "write_kib": 4096.0,
-                  "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
-                  "profile": "profiles/attention_fwd_bwd_c3.md"},
     ("c3", "bwd_dkdv"): {"bytes": 964896062, "fetch_kib": 340076.2, "write_kib": 262144.0,
                   "fetch_factor": 2.0, "write_factor": 1.0,
                   "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
@@ -69,7 +65,6 @@ TRAFFIC = {
 # The sources each kernel is built from: its counters stay valid while these are unchanged.
 KERNEL_SOURCES = {
     "fwd": ("fa_fwd.hip", "fa_common.h", "fa_launch.h"),
-    "bwd_preprocess": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
     "bwd_dkdv": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
     "bwd_dq": ("fa_bwd.hip", "fa_common.h", "fa_launch.h"),
 }
@@ -103,36 +98,48 @@ def gemm_unit(B, H, N, d, causal, lengths=None):
 
 
 def standard_attention(q, k, v, do, scale: float, causal: bool, reps: int = 3):
-    """Standard (materialising) attention on the same GPU, for comparison: S = scale Q K^T
-    and P = softmax(S) are written to HBM as full N x N matrices (bf16 GEMMs with fp32
-    accumulation via torch.matmul, softmax in fp32), and the backward is the textbook
-    chain rule on those stored matrices. Every matmul gets contiguous operands. Returns
-    fwd/bwd times (median of `reps`, HIP events on the current stream), the peak device
-    memory the two passes allocate, and O for a sanity check."""
+    """Standard attention on the same GPU, for comparison: the N x N matrices S, P and dP
+    are written to HBM and read back, as the pages describe the method being improved
+    upon. Plain PyTorch bf16: batched GEMMs (fp32 accumulation, bf16 results) and bf16
+    elementwise/softmax kernels, each operand laid out as its GEMM wants it before the
+    timed region (Q pre-scaled by the softmax scale, K^T, V^T, dO^T, Q^T contiguous), so
+    nothing is transposed or converted inside it. Per step:
+      forward   S = (scale Q) K^T            GEMM, writes S (bf16)
+                S[hidden] = -inf             in place, causal only (reads and writes S)
+                P = softmax(S)               reads S, writes P (bf16)
+                O = P V                      GEMM, reads P
+      backward  dV^T = dO^T P                GEMM, reads P
+                dP = dO V^T                  GEMM, writes dP (bf16)
+                D = rowsum(dO * O)           small
+                dS = P * (dP - D)            in place on dP (two passes: reads dP/P, writes dP)
+                dQ = scale dS K, dK^T = scale Q^T dS   GEMMs, read dS
+    Returns fwd/bwd times (median of `reps` after one untimed pass, HIP events on the
+    current stream), the peak device memory the two passes allocate, and O."""
     import torch
     B, N, H, d = q.shape
-    qh, kh, vh, doh = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v, do))  # (B, H, N, d)
-    kt = kh.transpose(-1, -2).contiguous()
-    vt = vh.transpose(-1, -2).contiguous()
+    bf = q.dtype
+    qh = (q.float() * scale).to(bf).permute(0, 2, 1, 3).contiguous()          # (B, H, N, d)
+    kh, vh, doh = (t.permute(0, 2, 1, 3).contiguous() for t in (k, v, do))
+    kt, vt, dot = (t.transpose(-1, -2).contiguous() for t in (kh, vh, doh))   # (B, H, d, N)
+    qt = q.permute(0, 2, 3, 1).contiguous()                                   # Q^T (B, H, d, N)
     mask = torch.ones(N, N, device=q.device, dtype=torch.bool).triu_(1) if causal else None
 
     def fwd():
-        s = torch.matmul(qh, kt).float().mul_(scale)
+        s = torch.matmul(qh, kt)
         if mask is not None:
             s.masked_fill_(mask, float("-inf"))
-        p = torch.softmax(s, dim=-1).to(q.dtype)
+        p = torch.softmax(s, dim=-1)
         del s
         return p, torch.matmul(p, vh)
 
     def bwd(p, o):
-        dv = torch.matmul(p.transpose(-1, -2).contiguous(), doh)
-        dp = torch.matmul(doh, vt).float()
-        dd = (doh.float() * o.float()).sum(-1, keepdim=True)
-        ds = (p.float() * (dp - dd)).to(q.dtype)
-        del dp
-        dq = torch.matmul(ds, kh).float().mul_(scale)
-        dk = torch.matmul(ds.transpose(-1, -2).contiguous(), qh).float().mul_(scale)
-        return dq, dk, dv
+        dvt = torch.matmul(dot, p)
+        dp = torch.matmul(doh, vt)
+        dd = (doh.float() * o.float()).sum(-1, keepdim=True).to(bf)
+        dp.sub_(dd).mul_(p)                        # dS, in place
+        dq = torch.matmul(dp, kh).mul_(scale)
+        dkt = torch.matmul(qt, dp).mul_(scale)
+        return dq, dkt, dvt
 
     stream = torch.cuda.current_stream()
     tf, tb = [], []
@@ -153,7 +160,14 @@ def standard_attention(q, k, v, do, scale: float, causal: bool, reps: int = 3):
         del p, grads
     peak = torch.cuda.max_memory_allocated() - base
     med = lambda x: sorted(x[1:])[len(x[1:]) // 2]
-    return {"fwd_ms": med(tf), "bwd_ms": med(tb), "peak_extra_bytes": int(peak)}, o.permute(0, 2, 1, 3)
+    # HBM bytes the N x N matrices alone force per step, counting each read or write of
+    # S, P, dP once (bf16): forward S write, S read and P write (softmax), P read (PV),
+    # plus a read and a write of S for the causal mask; backward P read (dV), dP write,
+    # dP read + write (- D), dP and P read + dP write (* P), dS read twice (dQ, dK).
+    nn = 2.0 * B * H * N * N
+    nxn = nn * ((4 + (2 if causal else 0)) + 9)
+    return {"fwd_ms": med(tf), "bwd_ms": med(tb), "peak_extra_bytes": int(peak),
+            "nxn_bytes_per_step": nxn, "passes": reps + 1}, o.permute(0, 2, 1, 3)
 
 
 def decode_bench(reps: int = 20):
@@ -326,6 +340,32 @@ def cpu_baseline(inp, w, budget_s: float):
     heads = [(b, h) for b in range(B) for h in range(H)]
     flops = 0.0
     done = 0
+    N0 = inp.q.shape[1]
+    if 8.0 * N0 * N0 > 4e9:
+        # One head's fp64 score matrix would exceed 4 GB (the long-context workload): time
+        # the oracle on 256 seeded query rows per head instead, O and dQ of those rows
+        # (forward 2 and dQ 3 products of 256 x N x d: 10 * 256 * N * d FLOP per head).
+        import workloads as W
+        rows = W.sample_rows(w.seed, N0, 256)
+        t0 = time.perf_counter()
+        for b, h in heads:
+            q, k, v, do = (oracle.to_f64(t[b, :, h, :]) for t in (inp.q, inp.k, inp.v, inp.do))
+            oracle.forward_rows(q, k, v, w.scale, w.causal, rows)
+            oracle.backward_query_rows(q, k, v, do, w.scale, w.causal, rows)
+            flops += 10.0 * rows.size * N0 * q.shape[1]
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {
+            "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"256 seeded query rows (O and dQ) of {done} of {len(heads)} heads of {w.name}, fp64, "
+                      f"{dt:.1f} s wall; FLOPs counted for those rows only (10 x 256 x N x d per head)",
+            "host_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "blas": [{"vendor": i.get("internal_api"), "version": i.get("version"),
+                      "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
+                     for i in blas],
+        }
     t0 = time.perf_counter()
     for b, h in heads:
         q, k, v, do = (oracle.to_f64(t[b, :, h, :]) for t in (inp.q, inp.k, inp.v, inp.do))
@@ -415,21 +455,19 @@ def main(argv=None) -> int:
         check(fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
                         w.scale, causal, cup, T, dt_code, sp), "fa_fwd")
 
-    def k_pre():
-        check(fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N,
-                                   d, w.scale, cup, T, dt_code, sp), "fa_bwd_preprocess")
+    def k_dq_stats():
+        check(fa.fa_bwd_dq_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), ws.data_ptr(), ws_bytes, dq.data_ptr(), B, H, N, d, w.scale, causal,
+                                 cup, T, dt_code, sp), "fa_bwd_dq_stats")
 
     def k_dkdv():
         check(fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              ws.data_ptr(), ws_bytes, dk.data_ptr(), dv.data_ptr(), B, H, N, d, w.scale,
                              causal, cup, T, dt_code, sp), "fa_bwd_dkdv")
 
-    def k_dq():
-        check(fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                           ws.data_ptr(), ws_bytes, dq.data_ptr(), B, H, N, d, w.scale, causal, cup, T,
-                           dt_code, sp), "fa_bwd_dq")
-
-    kernels = [("fwd", k_fwd), ("bwd_preprocess", k_pre), ("bwd_dkdv", k_dkdv), ("bwd_dq", k_dq)]
+    # The step: the forward, then the backward as fa_bwd runs it (the dQ pass, which also
+    # forms the row statistics, then dK/dV), each stage timed on its own.
+    kernels = [("fwd", k_fwd), ("bwd_dq", k_dq_stats), ("bwd_dkdv", k_dkdv)]
     if a.calibrate_copy_mib > 0:
         # The library's copy kernel (16-byte loads and stores per lane, like the kernels'
         # tile copies): it reads and writes calibrate_copy_mib MiB per launch, the known
@@ -474,8 +512,8 @@ def main(argv=None) -> int:
 
     unit = gemm_unit(B, H, N, d, w.causal, inp.lengths)
     fwd_fl, bwd_fl = 2 * unit, 5 * unit
-    algo = {"fwd": 2 * unit, "bwd_preprocess": 0.0, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
-    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    algo = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    bwd_ms = per["bwd_dkdv"] + per["bwd_dq"]
     value = (fwd_fl + bwd_fl) / (step_ms * 1e-3) / 1e12
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
     achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
@@ -528,6 +566,10 @@ def main(argv=None) -> int:
         # The same step with standard attention; its memory is what this library avoids.
         log("bench: standard attention (materialised scores) for comparison")
         st, o_std = standard_attention(q, k, v, do, w.scale, bool(w.causal))
+        e = q.element_size()
+        # this library's operand bytes per step: forward reads Q, K, V and writes O, LSE;
+        # backward reads Q, K, V, O, dO (+ statistics) and writes dQ, dK, dV
+        ours_bytes = (4 + 8) * B * N * H * d * e + 16 * B * H * N
         ours_fwd, ours_bwd = per["fwd"], bwd_ms
         out["standard_attention"] = {
             "fwd_ms": round(st["fwd_ms"], 4), "bwd_ms": round(st["bwd_ms"], 4),
@@ -535,6 +577,11 @@ def main(argv=None) -> int:
             "peak_extra_gib": round(st["peak_extra_bytes"] / 2**30, 2),
             "ours_workspace_gib": round(ws_bytes / 2**30, 4),
             "o_max_abs_diff": round(float((o_std.float() - o.float()).abs().max()), 4),
+            "nxn_bytes_per_step": st["nxn_bytes_per_step"],
+            "ours_operand_bytes_per_step": ours_bytes,
+            "dispatch_passes": st["passes"],
+            "note": "bf16 PyTorch: S, P, dP materialised in HBM; operand layouts prepared outside the "
+                    "timed region; Q pre-scaled in bf16",
         }
         del o_std
         torch.cuda.empty_cache()

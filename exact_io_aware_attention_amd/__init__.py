@@ -3,7 +3,7 @@
 A thin Python binding over ``libfa.so``, whose C ABI is declared in ``include/fa.h``.
 The raw entry points keep the C names and take integer device pointers:
 
-    fa_fwd, fa_bwd, fa_bwd_noalloc, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq,
+    fa_fwd, fa_bwd, fa_bwd_noalloc, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_stats,
     fa_bwd_workspace_bytes, fa_fwd_decode, fa_fwd_decode_workspace_bytes, fa_fwd_fp8, fa_strerror
 
 ``forward``, ``backward``, ``decode`` and ``forward_fp8`` marshal torch tensors (device memory and the current
@@ -69,6 +69,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.restype = i32
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
     lib.fa_bwd_dq.restype = i32
+    lib.fa_bwd_dq_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32,
+                                    vp]
+    lib.fa_bwd_dq_stats.restype = i32
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
@@ -141,6 +144,14 @@ def fa_bwd_dq(q: int, k: int, v: int, dout: int, lse: int, workspace: int, works
     return load_library().fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen,
                                     head_dim, softmax_scale, int(causal), cu_seqlens, total_tokens, dtype,
                                     stream)
+
+
+def fa_bwd_dq_stats(q: int, k: int, v: int, o: int, dout: int, lse: int, workspace: int, workspace_bytes: int,
+                    dq: int, batch: int, heads: int, seqlen: int, head_dim: int, softmax_scale: float, causal: int,
+                    cu_seqlens: Optional[int], total_tokens: int, dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd_dq_stats(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, batch, heads,
+                                          seqlen, head_dim, softmax_scale, int(causal), cu_seqlens, total_tokens,
+                                          dtype, stream)
 
 
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen: int, head_dim: int, varlen: int,

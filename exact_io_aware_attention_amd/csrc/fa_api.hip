@@ -263,6 +263,36 @@ FA_EXPORT int fa_bwd_dq(const void* q, const void* k, const void* v, const void*
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dq_bf16(pr) : fa::launch_bwd_dq_fp32(pr));
 }
 
+FA_EXPORT int fa_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* workspace, size_t workspace_bytes, void* dq, int batch,
+                              int heads, int seqlen, int head_dim, float softmax_scale, int causal,
+                              const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(dout) || !aligned(lse) || !aligned(dq))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale, causal,
+                           cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK || pr.total_tokens == 0) return st;
+  if (dtype == FA_DTYPE_FP32) {
+    // fp32: the statistics pass, then the dQ pass that reads them
+    const int r = fa_bwd_preprocess(o, dout, lse, workspace, workspace_bytes, batch, heads, seqlen, head_dim,
+                                    softmax_scale, cu_seqlens, total_tokens, dtype, stream);
+    if (r != FA_OK) return r;
+    return fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen, head_dim,
+                     softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+  }
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.o = o;
+  pr.dout = dout;
+  pr.lse = lse;
+  pr.dq = dq;
+  pr.stream = static_cast<hipStream_t>(stream);
+  return status_of(fa::launch_bwd_dq_stats_bf16(pr));
+}
+
 FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
            int seqlen, int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,
@@ -276,14 +306,12 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale,
                            causal, cu_seqlens, total_tokens, dtype);
   if (st != FA_OK || pr.total_tokens == 0) return st;
-  int r = fa_bwd_preprocess(o, dout, lse, workspace, workspace_bytes, batch, heads, seqlen, head_dim,
-                            softmax_scale, cu_seqlens, total_tokens, dtype, stream);
+  // The dQ pass forms the row statistics as it goes; the dK/dV kernel reads them.
+  const int r = fa_bwd_dq_stats(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen,
+                                head_dim, softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
   if (r != FA_OK) return r;
-  r = fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, batch, heads, seqlen, head_dim,
-                  softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
-  if (r != FA_OK) return r;
-  return fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, batch, heads, seqlen, head_dim,
-                   softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
+  return fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, batch, heads, seqlen, head_dim,
+                     softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
 }
 
 FA_EXPORT int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,

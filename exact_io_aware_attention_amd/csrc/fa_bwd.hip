@@ -20,6 +20,9 @@
 //             over four LDS buffers; at 64 two waves share each SIMD instead.
 //   bwd_dq    the dQ accumulation pass: one workgroup per (sequence, head, 128-query
 //             tile), dQ^T += K^T dS^T over the key tiles, with one query per MFMA column.
+//             Its STATS form also computes the row statistics of bwd_pre for its own
+//             queries (it loads their dO rows anyway) and runs first, so the backward
+//             is two kernels: the dQ pass with the statistics, then bwd_dkdv.
 // There are no atomics, so the result is bitwise reproducible run to run.
 #include <type_traits>
 
@@ -38,7 +41,8 @@ struct BwdParams {
   const float* lse;
   const float* dvec;
   const float* mneg;  // -LSE / scale (lse layout)
-  float* dvec_out;
+  float* dvec_out;  // the dQ pass that forms the statistics writes D here ...
+  float* mneg_out;  // ... and -LSE / scale here
   u16* dq;
   u16* dk;
   u16* dv;
@@ -934,7 +938,23 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
 
 // One query tile of one (sequence, head) of the dQ pass. The two LDS buffers are free
 // again when it returns (its last step ends in a barrier).
-template <int D, bool CAUSAL, bool VARLEN, bool DESC = false>
+// Sum of the elementwise products of eight bf16 pairs, in fp32.
+__device__ __forceinline__ float dot8_bf16(const bf16x8& x, const bf16x8& y, float acc) {
+  const u32x4 a = __builtin_bit_cast(u32x4, x), b = __builtin_bit_cast(u32x4, y);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+    acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+
+// One query tile of the dQ pass. With STATS the tile also forms its queries' row
+// statistics, D_i = sum_k dO_ik O_ik (from the stored O, whose row the lane pair loads
+// beside dO) and -LSE_i / scale, and writes both to the workspace for the dK/dV kernel
+// that runs next: every query row belongs to exactly one tile, so the separate
+// statistics pass is not needed.
+template <int D, bool CAUSAL, bool VARLEN, bool STATS, bool DESC = false>
 __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
                                          u16* buf1) {
 #if __HIP_DEVICE_COMPILE__
@@ -962,8 +982,25 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
     st.qf[s] = qi < len ? ld16(p.q + off) : zero_bf16x8();
     st.dof[s] = qi < len ? ld16(p.dout + off) : zero_bf16x8();
   }
-  st.lse2 = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] * kLog2e : INFINITY;
-  st.dd = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
+  const float lse = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] : INFINITY;
+  st.lse2 = lse * kLog2e;
+  if constexpr (STATS) {
+    // lanes l and l ^ 32 hold the two halves of the row (head-dim 16 s + 8 g + 0..7)
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 o8 = qi < len ? ld16(p.o + base + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
+      part = dot8_bf16(st.dof[s], o8, part);
+    }
+    st.dd = pair_sum(part);
+    if (g == 0 && qi < len) {
+      const size_t si = stat_index<VARLEN>(p, b, h, start, qi);
+      p.dvec_out[si] = st.dd;
+      p.mneg_out[si] = -lse / p.scale;
+    }
+  } else {
+    st.dd = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
+  }
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) st.dqT[bb] = f32x16{};
 
@@ -1026,7 +1063,7 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
 // query tiles nt-1-i and i, so every workgroup visits the same number of key tiles, the
 // second tile's keys in descending order (co-resident workgroups then read the same key
 // tile at the same step; see the forward kernel).
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool STATS>
 __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p) {
   using L = DqLds<D>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
@@ -1047,11 +1084,11 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
   if (CAUSAL) {
     const int t_hi = nt - 1 - slot;
     if (t_hi < slot) return;
-    dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, t_hi, buf0, buf1);
-    if (slot < t_hi) dq_qtile<D, CAUSAL, VARLEN, true>(p, b, h, start, len, slot, buf0, buf1);
+    dq_qtile<D, CAUSAL, VARLEN, STATS>(p, b, h, start, len, t_hi, buf0, buf1);
+    if (slot < t_hi) dq_qtile<D, CAUSAL, VARLEN, STATS, true>(p, b, h, start, len, slot, buf0, buf1);
   } else {
     if (slot >= nt) return;
-    dq_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);
+    dq_qtile<D, CAUSAL, VARLEN, STATS>(p, b, h, start, len, slot, buf0, buf1);
   }
 }
 
@@ -1068,6 +1105,7 @@ BwdParams make_params(const Problem& pr) {
   p.dvec = pr.dvec;
   p.mneg = pr.mneg;
   p.dvec_out = pr.dvec;
+  p.mneg_out = pr.mneg;
   p.dq = static_cast<u16*>(pr.dq);
   p.dk = static_cast<u16*>(pr.dk);
   p.dv = static_cast<u16*>(pr.dv);
@@ -1106,15 +1144,21 @@ hipError_t launch_dkdv_t(const Problem& pr) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
-hipError_t launch_dq_t(const Problem& pr) {
+template <int D, bool CAUSAL, bool VARLEN, bool STATS>
+hipError_t launch_dq_any(const Problem& pr) {
   BwdParams p = make_params(pr);
   const int n_qtiles = (pr.seqlen + kDqBR - 1) / kDqBR;
   p.n_tiles = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // workgroup slots per (sequence, head)
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, VARLEN>),
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, VARLEN, STATS>),
                      dim3((unsigned)(p.n_tiles * pr.batch * pr.heads)), dim3(kDqThreads), 0, pr.stream, p);
   return hipGetLastError();
 }
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_dq_t(const Problem& pr) { return launch_dq_any<D, CAUSAL, VARLEN, false>(pr); }
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_dq_stats_t(const Problem& pr) { return launch_dq_any<D, CAUSAL, VARLEN, true>(pr); }
 
 }  // namespace
 
@@ -1126,5 +1170,7 @@ hipError_t launch_bwd_pre(const Problem& pr, bool fp32) {
 hipError_t launch_bwd_dkdv_bf16(const Problem& p) { FA_DISPATCH(launch_dkdv_t, p); }
 
 hipError_t launch_bwd_dq_bf16(const Problem& p) { FA_DISPATCH(launch_dq_t, p); }
+
+hipError_t launch_bwd_dq_stats_bf16(const Problem& p) { FA_DISPATCH(launch_dq_stats_t, p); }
 
 }  // namespace fa

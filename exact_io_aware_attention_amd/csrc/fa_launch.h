@@ -35,6 +35,8 @@ hipError_t launch_fwd_fp32(const Problem& p);
 hipError_t launch_bwd_pre(const Problem& p, bool fp32);   // D = rowsum(dO * O), -LSE / scale
 hipError_t launch_bwd_dkdv_bf16(const Problem& p);
 hipError_t launch_bwd_dq_bf16(const Problem& p);
+// The dQ pass that also writes the row statistics (p.dvec, p.mneg) from p.o, p.dout, p.lse.
+hipError_t launch_bwd_dq_stats_bf16(const Problem& p);
 hipError_t launch_bwd_dkdv_fp32(const Problem& p);
 hipError_t launch_bwd_dq_fp32(const Problem& p);
 

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kUbThreads) void ub_lds_kernel(float* __restrict__ 
     for (int i = 0; i < iters; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (((i * 8 + j) & 7) * 16) * P + 16 * (j & 3));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (((i * 3 + j) & 7) * 16) * P + 16 * (j & 3));
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
       }
   } else {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kUbThreads) void ub_lds_kernel(float* __restrict__ 
     for (int i = 0; i < iters; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bf16x8 v = lds_tr_operand(lds, P, ((i * 8 + j) & 7) * 16, 32 * (j & 3), lane);
+        const bf16x8 v = lds_tr_operand(lds, P, ((i * 3 + j) & 7) * 16, 32 * (j & 3), lane);
         const u32x4 u = __builtin_bit_cast(u32x4, v);
         acc ^= u[0] ^ u[1] ^ u[2] ^ u[3];
       }

@@ -101,13 +101,13 @@ size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
  * Backward pass for the loss gradient dout = dL/dO. Reads q, k, v, o, dout (as written
  * by fa_fwd and the caller) and lse (from fa_fwd); writes dq, dk, dv in the dtype and
  * layout of q. P is recomputed tile by tile from lse, never stored ("Recalcular en vez
- * de guardar"). Three kernels run on `stream` (the stages below, in order):
- *   1. D_i = rowsum(dO * O) and -LSE_i / softmax_scale for every query row, into the
- *      workspace;
- *   2. one workgroup per (sequence, head, key tile) accumulating dK and dV on chip
- *      while it walks the query tiles;
- *   3. the dQ accumulation pass: one workgroup per (sequence, head, query tile)
- *      accumulating dQ on chip while it walks the key tiles.
+ * de guardar"). Two stages run on `stream`, in order (see below):
+ *   1. fa_bwd_dq_stats: the dQ accumulation pass, one workgroup per (sequence, head,
+ *      query tile) accumulating dQ on chip while it walks the key tiles; it also forms
+ *      D_i = rowsum(dO * O) and -LSE_i / softmax_scale of its query rows into the
+ *      workspace (bf16: one kernel; fp32: fa_bwd_preprocess, then fa_bwd_dq);
+ *   2. fa_bwd_dkdv: one workgroup per (sequence, head, key tile) accumulating dK and dV
+ *      on chip while it walks the query tiles, reading those statistics.
  * No atomics: the result is bitwise deterministic from run to run.
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller; its contents on entry do not matter.
@@ -146,10 +146,12 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    int dtype, void* stream);
 
 /*
- * The three stages of fa_bwd, callable on their own (same arguments, conventions and
- * workspace as fa_bwd). fa_bwd_preprocess must complete before fa_bwd_dkdv and
- * fa_bwd_dq start; those two only read the workspace and may run concurrently on
- * different streams. Each enqueues exactly one kernel.
+ * The stages of the backward, callable on their own (same arguments, conventions and
+ * workspace as fa_bwd). The workspace statistics are written either by
+ * fa_bwd_preprocess or by fa_bwd_dq_stats, which must complete before fa_bwd_dkdv (and
+ * fa_bwd_dq) start; fa_bwd_dkdv and fa_bwd_dq only read the workspace and may run
+ * concurrently on different streams. Each enqueues exactly one kernel, except
+ * fa_bwd_dq_stats with FA_DTYPE_FP32 (two).
  *
  *  fa_bwd_preprocess: workspace <- D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale
  *    (fp32, lse layout each). D is the row sum of P * dP, the term the softmax backward
@@ -162,6 +164,19 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  *  fa_bwd_dq: dq. One workgroup per (sequence, head, query tile) accumulates dQ on chip
  *    while walking the key tiles, recomputing P from lse.
  */
+/*
+ *  fa_bwd_dq_stats: dq, and the workspace statistics of fa_bwd_preprocess (the same
+ *    values up to the order of the fp32 additions in D), in one pass: the dQ pass loads
+ *    the dO row of each of its queries anyway, and with the O row beside it forms D.
+ *    Every query row belongs to exactly one of its tiles. It is what fa_bwd runs first.
+ */
+int fa_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse,
+                    void* workspace, size_t workspace_bytes, void* dq,
+                    int batch, int heads, int seqlen, int head_dim,
+                    float softmax_scale, int causal,
+                    const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream);
+
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                       void* workspace, size_t workspace_bytes,
                       int batch, int heads, int seqlen, int head_dim, float softmax_scale,

@@ -34,7 +34,8 @@ def declared_functions(headers=(HEADER,)):
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_noalloc", "fa_bwd_preprocess",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_bwd_noalloc",
+                                    "fa_bwd_preprocess",
                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
                                     "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_strerror"]
 
@@ -147,6 +148,14 @@ def test_stage_argument_checks():
     assert fa.fa_bwd_dq(q=A, k=A, v=MIS, dout=A, lse=A, dq=A, **ws, **sc, **common) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_dq(q=A, k=A, v=A, dout=A, lse=A, dq=A, **ws, **dict(sc, causal=-1),
                         **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dq_stats(q=A, k=A, v=A, o=None, dout=A, lse=A, dq=A, **ws, **sc,
+                              **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dq_stats(q=A, k=A, v=A, o=MIS, dout=A, lse=A, dq=A, **ws, **sc,
+                              **common) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dq_stats(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, workspace=A, workspace_bytes=8,
+                              **sc, **common) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_dq_stats(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, **ws, softmax_scale=-1.0, causal=0,
+                              **common) == fa.FA_ERR_INVALID_ARG
 
 
 def test_workspace_size():

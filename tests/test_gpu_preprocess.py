@@ -1,6 +1,8 @@
-"""fa_bwd_preprocess through the C ABI: the workspace it writes (D_i = sum_k dO_ik O_ik
-of the stored O, then -LSE_i / scale, each an fp32 array in the LSE layout starting on a
-256-byte boundary) against the oracle's backward statistics, element by element.
+"""The backward's row statistics through the C ABI: the workspace that fa_bwd_preprocess,
+and the dQ pass that forms them itself (fa_bwd_dq_stats, what fa_bwd runs), write
+(D_i = sum_k dO_ik O_ik of the stored O, then -LSE_i / scale, each an fp32 array in the
+LSE layout starting on a 256-byte boundary) against the oracle's backward statistics,
+element by element.
 
 Bound for D: the kernel forms exact products of bf16 values and adds them in fp32, so
 |D - D_ref| <= n u sum_k |dO_ik O_ik| with n = head_dim terms and u = 2^-24; 1e-5 covers
@@ -32,10 +34,11 @@ def _stat_bytes(heads, tokens):
     return (heads * tokens * 4 + 255) // 256 * 256
 
 
+@pytest.mark.parametrize("producer", ["preprocess", "dq_stats"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_preprocess_matches_oracle(case):
+def test_preprocess_matches_oracle(case, producer):
     label, dtype, B, N, H, d, cu = case
-    print(f"preprocess {label}", flush=True)
+    print(f"statistics from {producer}: {label}", flush=True)
     g = torch.Generator().manual_seed(77 + N + H)
     T = cu[-1] if cu is not None else B * N
     shape = (T, H, d) if cu is not None else (B, N, H, d)
@@ -50,9 +53,18 @@ def test_preprocess_matches_oracle(case):
     od, dod, lsed = o.cuda(), do.cuda(), lse.cuda()
     cud = torch.tensor(cu, dtype=torch.int32, device="cuda") if cu is not None else None
     code = fa.FA_DTYPE_BF16 if dtype == torch.bfloat16 else fa.FA_DTYPE_FP32
-    st = fa.fa_bwd_preprocess(od.data_ptr(), dod.data_ptr(), lsed.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d,
-                              scale, cud.data_ptr() if cud is not None else None, T, code,
-                              torch.cuda.current_stream().cuda_stream)
+    cup = cud.data_ptr() if cud is not None else None
+    sp = torch.cuda.current_stream().cuda_stream
+    if producer == "preprocess":
+        st = fa.fa_bwd_preprocess(od.data_ptr(), dod.data_ptr(), lsed.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N,
+                                  d, scale, cup, T, code, sp)
+    else:
+        # the dQ pass needs Q, K, V too; only the statistics it leaves are checked here
+        q, k, v = (torch.randn(shape, generator=g).to(dtype).cuda() for _ in range(3))
+        dq = torch.empty_like(q)
+        st = fa.fa_bwd_dq_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), od.data_ptr(), dod.data_ptr(),
+                                lsed.data_ptr(), ws.data_ptr(), ws_bytes, dq.data_ptr(), B, H, N, d, scale, 1, cup,
+                                T, code, sp)
     assert st == fa.FA_OK
     torch.cuda.synchronize()
     raw = ws.cpu()
