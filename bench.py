@@ -41,23 +41,23 @@ BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 MFMA FLOP per clock per compute unit (
 TARGET_FRAC = {"fwd": 0.50, "bwd": 0.35}
 CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 
-# HBM traffic per launch of a kernel, from two rocprofv3 --pmc passes over this script
-# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) on the named workload, each scaled by
-# the ratio that the same counter shows for a copy kernel of known size run in the same
-# process (--calibrate-copy-mib). Reported only while the kernel sources still hash to
-# the value they had when the counters were taken; otherwise null.
+# Memory traffic per launch of a kernel (bytes between L2 and the memory fabric: HBM and
+# the Infinity Cache in front of it, which these counters cannot tell apart), from two
+# rocprofv3 --pmc passes over this script on the named workload: reads as the sum over
+# TCC_EA0_RDREQ_32B/_64B/_128B of requests x size, writes as WRITE_SIZE. The same passes
+# count the library's copy kernel (--calibrate-copy-mib 1024) at 1.0000 GiB read and
+# 1.0000 GiB written per launch, so the scale factors are 1. (FETCH_SIZE counts a 128-byte
+# read request as 64 bytes, half of these kernels' reads.) Reported only while the
+# kernel's sources hash to the value they had when the counters were taken; else null.
 TRAFFIC = {
-    ("c3", "fwd"): {"bytes": 724759552, "fetch_kib": 287332.9, "write_kib": 133120.0,
-                  "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
+    ("c3", "fwd"): {"read_bytes": 505197344, "write_bytes": 136314880, "factor": 1.0,
+                  "sources_sha256": "419c5cb1386b41dba2cc06e180c9be626171fd3ceb296032a92504958ab730d5",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dkdv"): {"bytes": 964896062, "fetch_kib": 340076.2, "write_kib": 262144.0,
-                  "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
+    ("c3", "bwd_dq"): {"read_bytes": 790774784, "write_bytes": 138412032, "factor": 1.0,
+                  "sources_sha256": "3df7167c9041ed577d7ab4db7a7172467bee9eb54e436357c08b108c78c6f1cb",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
-    ("c3", "bwd_dq"): {"bytes": 898215941, "fetch_kib": 373054.3, "write_kib": 131072.0,
-                  "fetch_factor": 2.0, "write_factor": 1.0,
-                  "sources_sha256": "864d63ae2d056263a4906f8659a463a4b0d4130391f1d42b2dfc0f7678990e44",
+    ("c3", "bwd_dkdv"): {"read_bytes": 688679232, "write_bytes": 268435456, "factor": 1.0,
+                  "sources_sha256": "3df7167c9041ed577d7ab4db7a7172467bee9eb54e436357c08b108c78c6f1cb",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
 }
 
@@ -313,12 +313,13 @@ def ceilings(reps: int = 5):
         "fma_fp32_tflops": round(2 * lane_ops / (t_fma * 1e-3) / 1e12, 1),
         "fma_lane_ops_per_clk_cu": round(lane_ops / (t_fma * 1e-3) / clk_hz / cus, 2),
         "copy_gbs": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
-        # LDS operand reads per clock per CU (wave instructions): what bounds an MFMA whose
-        # operand comes from LDS (one row read, or two transpose reads, per MFMA)
-        "lds_b128_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldsr * 1e-3) / clk_hz / cus, 4),
-        "lds_tr16_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldst * 1e-3) / clk_hz / cus, 4),
-        "lds_b128_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldsr * 1e-3) / 1e12, 1),
-        "lds_tr16_tbs": round(lblocks * 4 * liters * 8 * 512 / (t_ldst * 1e-3) / 1e12, 1),
+        # LDS operand reads (1 KiB per wave each: one ds_read_b128, or two 512-byte
+        # ds_read_b64_tr_b16) per clock per CU and in bytes per second: what bounds an
+        # MFMA whose 32x16 bf16 operand comes from LDS
+        "lds_row_operands_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldsr * 1e-3) / clk_hz / cus, 4),
+        "lds_tr_operands_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldst * 1e-3) / clk_hz / cus, 4),
+        "lds_row_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldsr * 1e-3) / 1e12, 1),
+        "lds_tr_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldst * 1e-3) / 1e12, 1),
         "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
                "lds_rows": round(t_ldsr, 4), "lds_tr": round(t_ldst, 4)},
         "note": "rates per clock use the reported maximum clock; the clock under load may be lower",
@@ -366,9 +367,20 @@ def cpu_baseline(inp, w, budget_s: float):
                       "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
                      for i in blas],
         }
+    if inp.cu_seqlens is not None:
+        # packed batch: whole (sequence, head) pairs, causal within each sequence
+        cu = inp.cu_seqlens.tolist()
+        H = inp.q.shape[1]
+        heads = [(s, h) for s in range(len(cu) - 1) for h in range(H)]
+
+        def view(t, s, h):
+            return oracle.to_f64(t[cu[s]:cu[s + 1], h, :])
+    else:
+        def view(t, b, h):
+            return oracle.to_f64(t[b, :, h, :])
     t0 = time.perf_counter()
     for b, h in heads:
-        q, k, v, do = (oracle.to_f64(t[b, :, h, :]) for t in (inp.q, inp.k, inp.v, inp.do))
+        q, k, v, do = (view(t, b, h) for t in (inp.q, inp.k, inp.v, inp.do))
         oracle.head_forward(q, k, v, w.scale, w.causal)
         oracle.head_backward(q, k, v, do, w.scale, w.causal)
         N, d = q.shape
@@ -382,7 +394,8 @@ def cpu_baseline(inp, w, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} (batch, head) pairs of {w.name}, fp64 forward + backward "
+        "sample": f"{done} of {len(heads)} ({'sequence' if inp.cu_seqlens is not None else 'batch'}, head) pairs "
+                  f"of {w.name}, fp64 forward + backward "
                   f"(oracle materialises the full N x N scores), {dt:.1f} s wall",
         "host_cpus": len(os.sched_getaffinity(0)),
         "os_cpu_count": os.cpu_count(),
@@ -513,6 +526,11 @@ def main(argv=None) -> int:
     unit = gemm_unit(B, H, N, d, w.causal, inp.lengths)
     fwd_fl, bwd_fl = 2 * unit, 5 * unit
     algo = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    # each operand read once and each result written once (X = one (tokens, heads, d) tensor,
+    # S = one fp32 row statistic per (head, token))
+    X = T * H * d * q.element_size()
+    S = T * H * 4
+    algo_bytes = {"fwd": 3 * X + X + S, "bwd_dq": 5 * X + S + X + 2 * S, "bwd_dkdv": 4 * X + 2 * S + 2 * X}
     bwd_ms = per["bwd_dkdv"] + per["bwd_dq"]
     value = (fwd_fl + bwd_fl) / (step_ms * 1e-3) / 1e12
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
@@ -548,14 +566,18 @@ def main(argv=None) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if tr is None else tr["bytes"],
+            "traffic": None if tr is None else tr["read_bytes"] + tr["write_bytes"],
         },
     }
     if tr is not None:
+        tb = tr["read_bytes"] + tr["write_bytes"]
         out["roofline"]["traffic_detail"] = {
-            "hbm_bytes_per_launch": tr["bytes"], "fetch_kib": tr["fetch_kib"], "write_kib": tr["write_kib"],
-            "fetch_factor": tr["fetch_factor"], "write_factor": tr["write_factor"],
-            "achieved_hbm_gbs": round(tr["bytes"] / (per[dom] * 1e-3) / 1e9, 1),
+            "fabric_bytes_per_launch": tb, "read_bytes": tr["read_bytes"], "write_bytes": tr["write_bytes"],
+            "counter_scale_factor": tr["factor"],
+            "algorithmic_bytes_per_launch": algo_bytes[dom],
+            "ratio_to_algorithmic": round(tb / algo_bytes[dom], 3),
+            "achieved_gbs": round(tb / (per[dom] * 1e-3) / 1e9, 1),
+            "note": "bytes between L2 and the memory fabric (HBM plus the Infinity Cache in front of it)",
             "profile": tr["profile"]}
     need = 3 * B * H * N * N * 4  # fp32 scores + bf16 copies, roughly
     total_mem = torch.cuda.get_device_properties(0).total_memory
@@ -602,7 +624,7 @@ def main(argv=None) -> int:
     if not a.no_fp8:
         log("bench: 8-bit forward")
         out["fp8_forward"] = fp8_bench(batch=a.batch, seqlen=a.seqlen)
-    if a.cpu_budget > 0 and w.varlen is False:
+    if a.cpu_budget > 0:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)
     else:
