@@ -257,6 +257,39 @@ def fp8_bench(reps: int = 20, batch=None, seqlen=None):
     return res
 
 
+def atomic_bwd_bench(fa, tensors, dims, det_ms: float, reps: int = 10):
+    """fa_bwd_atomic (dQ by fp32 atomics from the dK/dV kernel, then a conversion) on the
+    step's inputs, against the deterministic backward's time: the measured alternative to
+    the separate dQ pass (head_dim 128, bf16 only)."""
+    import torch
+    q, k, v, o, lse, do, cup = tensors
+    B, H, N, d, T, scale, causal, sp = dims
+    wsb = fa.fa_bwd_atomic_workspace_bytes(B, H, N, d, int(cup is not None), T)
+    ws = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    g = [torch.empty_like(q) for _ in range(3)]
+
+    def call():
+        st = fa.fa_bwd_atomic(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              g[0].data_ptr(), g[1].data_ptr(), g[2].data_ptr(), ws.data_ptr(), wsb, B, H, N, d, scale,
+                              causal, cup, T, fa.FA_DTYPE_BF16, sp)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_bwd_atomic")
+    for _ in range(3):
+        call()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": round(ms, 4), "deterministic_ms": round(det_ms, 4), "ratio_to_deterministic": round(ms / det_ms, 3),
+            "workspace_gib": round(wsb / 2**30, 3),
+            "note": "fa_bwd_atomic: row statistics + accumulator clear, the fused dK/dV/dQ kernel, dQ conversion"}
+
+
 def ceilings(reps: int = 5):
     """The device's own figures and measured ceilings: compute units and maximum engine
     clock as the HIP runtime reports them (the dense bf16 MFMA peak follows as CUs x 4096
@@ -420,6 +453,8 @@ def main(argv=None) -> int:
                     help="skip the measured ceilings (MFMA loop, exponential and FMA rates, copy)")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-attention comparison (materialised N x N scores)")
+    ap.add_argument("--no-atomic", action="store_true",
+                    help="skip timing fa_bwd_atomic (dQ by fp32 atomics) beside the deterministic backward")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the warmup, run the library's copy kernel over this many MiB, three times, "
                          "as the known-size reference for the byte counters")
@@ -607,6 +642,10 @@ def main(argv=None) -> int:
         }
         del o_std
         torch.cuda.empty_cache()
+    if not a.no_atomic and d == 128 and w.dtype == "bf16":
+        log("bench: backward with dQ by fp32 atomics (fa_bwd_atomic)")
+        out["bwd_atomic"] = atomic_bwd_bench(fa, (q, k, v, o, lse, do, cup),
+                                             (B, H, N, d, T, w.scale, causal, sp), bwd_ms)
     if not a.no_ceilings:
         log("bench: measured ceilings")
         c = ceilings()

@@ -3,8 +3,9 @@
 A thin Python binding over ``libfa.so``, whose C ABI is declared in ``include/fa.h``.
 The raw entry points keep the C names and take integer device pointers:
 
-    fa_fwd, fa_bwd, fa_bwd_noalloc, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_stats,
-    fa_bwd_workspace_bytes, fa_fwd_decode, fa_fwd_decode_workspace_bytes, fa_fwd_fp8, fa_strerror
+    fa_fwd, fa_bwd, fa_bwd_atomic, fa_bwd_noalloc, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_stats,
+    fa_bwd_workspace_bytes, fa_bwd_atomic_workspace_bytes, fa_fwd_decode, fa_fwd_decode_workspace_bytes,
+    fa_fwd_fp8, fa_strerror
 
 ``forward``, ``backward``, ``decode`` and ``forward_fp8`` marshal torch tensors (device memory and the current
 stream) into those calls; every step of the computation runs in the HIP kernels.
@@ -23,6 +24,7 @@ __all__ = [
     "FA_BWD_NOALLOC_MAX_SCRATCH", "fa_bwd_noalloc",
     "FA_DTYPE_BF16", "FA_DTYPE_FP32", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
+    "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
     "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_lds", "fa_ubench_copy",
 ]
@@ -60,6 +62,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_atomic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                  i32, i32, i32, i32, f32, i32, vp, i32, i32, vp]
+    lib.fa_bwd_atomic.restype = i32
+    lib.fa_bwd_atomic_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_bwd_atomic_workspace_bytes.restype = sz
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, i32,
                                    vp]
     lib.fa_bwd_noalloc.restype = i32
@@ -113,6 +120,20 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
                                  batch, heads, seqlen, head_dim, softmax_scale, int(causal),
                                  cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd_atomic(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+                  workspace: int, workspace_bytes: int, batch: int, heads: int, seqlen: int, head_dim: int,
+                  softmax_scale: float, causal: int, cu_seqlens: Optional[int], total_tokens: int,
+                  dtype: int, stream: Optional[int]) -> int:
+    return load_library().fa_bwd_atomic(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                                        batch, heads, seqlen, head_dim, softmax_scale, int(causal),
+                                        cu_seqlens, total_tokens, dtype, stream)
+
+
+def fa_bwd_atomic_workspace_bytes(batch: int, heads: int, seqlen: int, head_dim: int, varlen: int,
+                                  total_tokens: int) -> int:
+    return load_library().fa_bwd_atomic_workspace_bytes(batch, heads, seqlen, head_dim, int(varlen), total_tokens)
 
 
 def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, batch: int,
@@ -325,9 +346,10 @@ def forward(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
              cu_seqlens=None, max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, check_cu: bool = True) -> Tuple:
+             workspace=None, stream=None, check_cu: bool = True, deterministic: bool = True) -> Tuple:
     """(dQ, dK, dV) for the upstream gradient ``dout`` (see include/fa.h); ``check_cu`` as
-    in ``forward``."""
+    in ``forward``. ``deterministic=False`` calls fa_bwd_atomic (head_dim 128, bf16: one
+    pass with dQ accumulated by fp32 atomics, reproducible up to the last bits of dQ)."""
     import torch
     B, N, H, d, T = _shape(q, cu_seqlens, max_seqlen)
     varlen = cu_seqlens is not None
@@ -342,15 +364,17 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = fa_bwd_workspace_bytes(B, H, N, d, int(varlen), T)
+    size_fn, call, name = ((fa_bwd_workspace_bytes, fa_bwd, "fa_bwd") if deterministic else
+                           (fa_bwd_atomic_workspace_bytes, fa_bwd_atomic, "fa_bwd_atomic"))
+    ws_bytes = size_fn(B, H, N, d, int(varlen), T)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
     cu = cu_seqlens.data_ptr() if varlen else None
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), _workspace_bytes(workspace),
-                B, H, N, d, scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
+    st = call(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), _workspace_bytes(workspace),
+              B, H, N, d, scale, int(causal), cu, T, _dtype_code(q), _stream(stream))
     if st != FA_OK:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, name)
     return dq, dk, dv
 
 

@@ -314,6 +314,55 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
                      softmax_scale, causal, cu_seqlens, total_tokens, dtype, stream);
 }
 
+// fa_bwd_atomic's workspace: the statistics as in fa_bwd, then the fp32 dQ accumulator,
+// (heads * tokens + 64) rows of head_dim (the 64 extra rows take the zero terms of the
+// last query tile's rows past the end).
+size_t dqacc_bytes_for(int heads, long long tokens, int head_dim) {
+  return ((size_t)heads * (size_t)tokens + 64) * (size_t)head_dim * sizeof(float);
+}
+
+FA_EXPORT size_t fa_bwd_atomic_workspace_bytes(int batch, int heads, int seqlen, int head_dim, int varlen,
+                                               int total_tokens) {
+  const size_t stats = fa_bwd_workspace_bytes(batch, heads, seqlen, head_dim, varlen, total_tokens);
+  if (stats == 0) return 0;
+  const long long tokens = varlen ? (long long)total_tokens : (long long)batch * seqlen;
+  return stats + dqacc_bytes_for(heads, tokens, head_dim);
+}
+
+FA_EXPORT int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            int batch, int heads, int seqlen, int head_dim, float softmax_scale, int causal,
+                            const int32_t* cu_seqlens, int total_tokens, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(dout) || !aligned(lse) ||
+      !aligned(dq) || !aligned(dk) || !aligned(dv))
+    return FA_ERR_INVALID_ARG;
+  fa::Problem pr{};
+  const int st = check_bwd(pr, workspace, workspace_bytes, batch, heads, seqlen, head_dim, softmax_scale,
+                           causal, cu_seqlens, total_tokens, dtype);
+  if (st != FA_OK) return st;
+  if (head_dim != 128 || dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  const size_t stats = workspace_bytes_for(heads, pr.total_tokens);
+  if (workspace_bytes < stats + dqacc_bytes_for(heads, pr.total_tokens, head_dim)) return FA_ERR_WORKSPACE;
+  if (pr.total_tokens == 0) return FA_OK;
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.o = o;
+  pr.dout = dout;
+  pr.lse = lse;
+  pr.dq = dq;
+  pr.dk = dk;
+  pr.dv = dv;
+  pr.dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + stats);
+  pr.stream = static_cast<hipStream_t>(stream);
+  // Statistics (and the accumulator cleared), the fused kernel, then dQ from the accumulator.
+  hipError_t e = fa::launch_bwd_pre(pr, false);
+  if (e == hipSuccess) e = fa::launch_bwd_fused_bf16(pr);
+  if (e == hipSuccess) e = fa::launch_bwd_dq_convert(pr);
+  return status_of(e);
+}
+
 FA_EXPORT int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
                              const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int seqlen,
                              int head_dim, float softmax_scale, int causal, const int32_t* cu_seqlens,

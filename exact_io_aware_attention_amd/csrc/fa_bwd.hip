@@ -43,6 +43,7 @@ struct BwdParams {
   const float* mneg;  // -LSE / scale (lse layout)
   float* dvec_out;  // the dQ pass that forms the statistics writes D here ...
   float* mneg_out;  // ... and -LSE / scale here
+  float* dqacc;     // fused backward: fp32 dQ accumulator, (stat rows + 64) x D
   u16* dq;
   u16* dk;
   u16* dv;
@@ -115,8 +116,8 @@ constexpr int kPreTokens = 64;
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                       const float* __restrict__ lse, float* __restrict__ dvec,
-                                                      float* __restrict__ mneg, float scale, int H, int n_seq,
-                                                      int n_tiles) {
+                                                      float* __restrict__ mneg, float* __restrict__ zacc,
+                                                      float scale, int H, int n_seq, int n_tiles) {
   constexpr int LPR = D / 8;               // lanes per row
   constexpr int RPP = 256 / LPR;           // rows per pass
   constexpr int PASSES = kPreTokens / RPP;
@@ -155,6 +156,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
       dvec[base + t] = sd[t];
     else if (threadIdx.x < 2 * kPreTokens)
       mneg[base + t] = -lse[base + t] / scale;
+  }
+  if (zacc != nullptr) {
+    // The fused backward's dQ accumulator rows of these tokens start at zero (same row
+    // order as the statistics, D floats per row).
+    const int rows = min(kPreTokens, n_seq - n0);
+    f32x4* z = reinterpret_cast<f32x4*>(zacc + base * D);
+    for (int i = threadIdx.x; i < rows * (D / 4); i += 256) z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -580,6 +588,455 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int valid = len - wk0;
   store_staged_rows<D, 32>(stg, p.dk + base + (size_t)wk0 * stride, stride, valid, lane);
   store_staged_rows<D, 32>(stg + 32 * stage_pitch<D>(), p.dv + base + (size_t)wk0 * stride, stride, valid, lane);
+}
+
+// ------------------------------------------------------------------------ bwd_fused
+//
+// The head_dim-128 dK/dV kernel with the dQ product folded in: one pass over the key
+// tiles computes all five products (S, dP, dV, dK and dQ; the recomputation of P by
+// blocks in "Recalcular en vez de guardar", AI Atlas summary of the FlashAttention
+// paper), against seven in the two-kernel backward, at the price of fp32 atomics whose
+// order makes dQ reproducible only up to rounding.
+//
+// The dQ product contracts over keys, which a wave holds one per lane, so -dS changes
+// hands through LDS: after its softmax step every wave writes its 32 keys x 32 queries
+// of -dS (bf16, the values its own dK product uses) into an exchange tile, and after the
+// next workgroup barrier each wave computes -dQ / scale for the block's 32 queries and
+// its own 32-wide slice of head_dim over all 128 keys (8 MFMAs; one query per C row, one
+// head-dim column per lane, the K operands held in AGPRs since the prologue). The result
+// is added into an fp32 accumulator in global memory (B, H, N, D) / (H, T, D) with
+// global_atomic_add_f32, 128 contiguous bytes per half-wave; bwd_dq_convert scales it
+// and writes dQ. The accumulator is zeroed by the statistics kernel (bwd_pre) that runs
+// first.
+//
+// Schedule per 64-query tile t (blocks (t,0) and (t,1)), with X and Y the phases of the
+// dK/dV kernel:
+//   X(t,0)  write -dS(t,0) to E0[t % 2]   barrier t   Y(t,0) + atomics of dQ(t-2,1), dQ(t-1,0)
+//   X(t,1)  write -dS(t,1) to E1[t % 2]               Y(t,1) + MFMAs of dQ(t-1,1), dQ(t,0)
+// Each exchange slot is read between the barrier after its write and the one after that,
+// and rewritten only after the latter. Three Q/dO buffers (not four) leave room for the
+// four 8 KB exchange tiles; with three, the wait at every barrier is for all copies in
+// flight, so the atomics, issued right after the barrier, have a whole tile to complete
+// before the next wait.
+
+constexpr int kFzStages = 3;
+constexpr int kXq = 32;                 // queries per exchange-tile row
+constexpr int kXTile = kKvBK * kXq;     // elements of one exchange tile (8 KB)
+
+// Element offset of 4-element run `run` (queries 4 run .. 4 run + 3) of key row kk in an
+// exchange tile. Runs are swizzled by key, run ^ ((kk >> 2) & 7): a wave's writes (one
+// run per lane, 32 keys) and the transpose reads of the dQ product (4 keys x 32 queries
+// per 32 lanes) both fall on distinct banks.
+__device__ __forceinline__ int xch_elem(int kk, int run) { return kk * kXq + 4 * (run ^ ((kk >> 2) & 7)); }
+
+// This lane's -dS (db: key kk, queries 8 r4 + 4 g + 0..3 in registers 4 r4 .. 4 r4 + 3)
+// into exchange tile x, one 8-byte write per r4.
+__device__ __forceinline__ void xch_write(u16* x, const bf16x8 (&db)[2], int kk, int g) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const u32x4 u = __builtin_bit_cast(u32x4, db[r4 >> 1]);
+    *reinterpret_cast<u32x2*>(x + xch_elem(kk, 2 * r4 + g)) = u32x2{u[2 * (r4 & 1)], u[2 * (r4 & 1) + 1]};
+  }
+}
+
+// A operand of step s of a dQ product from exchange tile x: row m = query m of the block,
+// k-slots = keys 16 s + 4 g + {0..3, 8..11}, in the order of lds_tr_operand. The lane's
+// addresses depend on s only through 512 s and the swizzle bit s % 2: xo holds the
+// lane's element offsets for (s % 2, lo / hi read), set once by xch_lane_offsets.
+struct XchLane {
+  int o[4];
+};
+
+__device__ __forceinline__ XchLane xch_lane_offsets(int lane) {
+  const int i = lane & 15, G = lane >> 4;
+  const int kl = 4 * (G >> 1) + (i >> 2);  // key within the 16-key slice (lo read)
+  const int run = 4 * (G & 1) + (i & 3);
+  XchLane x;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    x.o[2 * par] = xch_elem(16 * par + kl, run);
+    x.o[2 * par + 1] = xch_elem(16 * par + kl + 8, run);
+  }
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 xch_operand(const u16* x, const XchLane& xo, int s) {
+  const u16* t = x + 16 * kXq * (s & ~1);
+  const i16x4 lo = ds_read_tr16(t + xo.o[2 * (s & 1)]);
+  const i16x4 hi = ds_read_tr16(t + xo.o[2 * (s & 1) + 1]);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// dQ MFMAs on AGPR accumulators with the K operand (B) in AGPRs too; the first step of a
+// block starts from zero. The wait states are those of mfma32_agpr.
+__device__ __forceinline__ void dq_mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "a"(b));
+}
+
+__device__ __forceinline__ void dq_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "a"(b));
+}
+
+__device__ __forceinline__ bf16x8 to_agpr(const bf16x8& x) {
+  bf16x8 y;
+  asm volatile("; K operand to AGPRs" : "=a"(y) : "0"(x));
+  return y;
+}
+
+__device__ __forceinline__ void agpr_acc_fence2(f32x16& a, f32x16& b) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a), "+a"(b));
+}
+
+// Adds v at byte offset off (this lane's, 32-bit) from the wave-uniform address base: the
+// uniform part stays in SGPRs (the atomic's scalar base), the lane part in one VGPR.
+__device__ __forceinline__ void atomic_add_f32(const char* base, uint32_t off, float v) {
+  __builtin_amdgcn_global_atomic_fadd_f32((__attribute__((address_space(1))) float*)(base + (uint64_t)off), v);
+}
+
+// Byte offset of register r's row from a dQ block's first row (C row crow_nat(r, g) minus
+// the lane group's 4 g, which is in the lane offset).
+template <int D>
+constexpr uint32_t dq_row_bytes(int r) { return (uint32_t)((8 * (r >> 2) + (r & 3)) * D * 4); }
+
+// Phase Y(t,0) of the fused kernel: kv_phase_y's 16 MFMAs for block cu, and the atomics
+// that add the two finished dQ blocks qa (first row at ga) and qb (at gb) into the
+// accumulator, two per step. Register r of lane group g holds query row crow_nat(r, g),
+// head-dim column 32 w + lr: byte offset dq_row_bytes(r) + loff from the block's first
+// row, with loff = 4 (4 g D + 32 w + lr).
+template <int D, bool NXT>
+__device__ __forceinline__ void fz_phase_y_atomics(KvState<D>& st, const u16* bc, int rc, const bf16x8 (&pb)[2],
+                                                   const bf16x8 (&db)[2], bf16x8 (&top)[kKvPf], const u16* bn, int rn,
+                                                   bf16x8 (&rop)[kKvPf], KvBlock& nx, f32x16& qa, const char* ga,
+                                                   f32x16& qb, const char* gb, uint32_t loff, int lane) {
+  constexpr int NT = D / 16, NB = D / 32, NY = 2 * NT;
+  static_assert(NY == 16, "two atomics per step cover the 16 registers of each block");
+  agpr_acc_fence2(qa, qb);
+#pragma unroll
+  for (int j = 0; j < NY; ++j) {
+    const bf16x8 a = top[j % kKvPf];
+    if (j + kKvPf < NY) top[j % kKvPf] = kv_tr_operand<D>(bc, rc, j + kKvPf, lane);
+    const int jj = j % NT;
+    if (j < NT)
+      kv_acc_mfma<D>(st.dvT[jj % NB], a, pb[jj / NB]);
+    else
+      kv_acc_mfma<D>(st.dkT[jj % NB], a, db[jj / NB]);
+    atomic_add_f32(ga + dq_row_bytes<D>(j), loff, qa[j]);
+    atomic_add_f32(gb + dq_row_bytes<D>(j), loff, qb[j]);
+    if constexpr (NXT) {
+      if (j >= NY - kKvPf) rop[j - (NY - kKvPf)] = kv_row_operand<D>(bn, rn, j - (NY - kKvPf), lane);
+      if (j >= NY - 8 && j < NY - 4) kv_init_dp<D>(nx, bn, rn, j - (NY - 8), lane >> 5);
+      if (j >= NY - 4) kv_init_s<D>(nx, bn, rn, j - (NY - 4), lane >> 5);
+    }
+    step_fence();
+  }
+}
+
+// Phase Y(t,1) of the fused kernel: kv_phase_y's 16 MFMAs for block cu interleaved with
+// the 16 MFMAs of two dQ blocks, qa from exchange tile xa and qb from xb (dQ step u:
+// block u % 2, key slice u / 2). Order: kv0 kv1 dq0 kv2 dq1 kv3 ... kv15 dq14 dq15, so
+// each dQ accumulator is updated every fourth MFMA; the dQ operands are read two dQ steps
+// ahead.
+template <int D, bool NXT>
+__device__ __forceinline__ void fz_phase_y_dq(KvState<D>& st, const u16* bc, int rc, const bf16x8 (&pb)[2],
+                                              const bf16x8 (&db)[2], bf16x8 (&top)[kKvPf], const u16* bn, int rn,
+                                              bf16x8 (&rop)[kKvPf], KvBlock& nx, const u16* xa, const u16* xb,
+                                              const XchLane& xo, const bf16x8 (&kq)[8], f32x16& qa, f32x16& qb,
+                                              int lane) {
+  constexpr int NT = D / 16, NB = D / 32, NY = 2 * NT;
+  static_assert(NY == 16, "16 dQ steps pair with the 16 dV / dK steps");
+  bf16x8 xop[2];
+  auto kv_step = [&](int j) {
+    const bf16x8 a = top[j % kKvPf];
+    if (j + kKvPf < NY) top[j % kKvPf] = kv_tr_operand<D>(bc, rc, j + kKvPf, lane);
+    const int jj = j % NT;
+    if (j < NT)
+      kv_acc_mfma<D>(st.dvT[jj % NB], a, pb[jj / NB]);
+    else
+      kv_acc_mfma<D>(st.dkT[jj % NB], a, db[jj / NB]);
+    if constexpr (NXT) {
+      if (j >= NY - kKvPf) rop[j - (NY - kKvPf)] = kv_row_operand<D>(bn, rn, j - (NY - kKvPf), lane);
+      if (j >= NY - 8 && j < NY - 4) kv_init_dp<D>(nx, bn, rn, j - (NY - 8), lane >> 5);
+      if (j >= NY - 4) kv_init_s<D>(nx, bn, rn, j - (NY - 4), lane >> 5);
+    }
+    step_fence();
+  };
+  auto dq_step = [&](int u) {
+    const bf16x8 a = xop[u & 1];
+    if (u + 2 < 16) xop[u & 1] = xch_operand(((u + 2) & 1) ? xb : xa, xo, (u + 2) >> 1);
+    f32x16& acc = (u & 1) ? qb : qa;
+    if (u < 2)
+      dq_mfma_first(acc, a, kq[u >> 1]);
+    else
+      dq_mfma(acc, a, kq[u >> 1]);
+    step_fence();
+  };
+  xop[0] = xch_operand(xa, xo, 0);
+  xop[1] = xch_operand(xb, xo, 0);
+  kv_step(0);
+#pragma unroll
+  for (int i = 1; i < NY; ++i) {
+    kv_step(i);
+    dq_step(i - 1);
+  }
+  dq_step(15);
+}
+
+// One workgroup per (sequence, head, 128-key tile); every wave walks the 64-query tiles
+// from the workgroup's first (under causal, the one holding its first key) to the last.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_fused_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "the fused backward is built for head_dim 128");
+  constexpr int BK = kKvBK, BQ = kKvBQ, NS = D / 16, NB = D / 32;
+  constexpr int S = kFzStages;
+  using L = KvLds<D>;
+  using Dma = TileDma<BQ, D, L::P, kKvWaves, true, 8, false>;  // statistics in the pads of Q rows 0..7
+  constexpr int KVP = D + 8;  // row pitch of the staged K/V rows: conflict-free row reads
+  // LDS: S tile buffers, then the four exchange tiles (E0[0], E0[1], E1[0], E1[1]). In the
+  // prologue K is staged in buffer 2 and V over the exchange tiles (and beyond).
+  constexpr int XOFF = S * L::BUF;
+  constexpr int LDS_ELEMS = XOFF + (4 * kXTile > BK * KVP ? 4 * kXTile : BK * KVP);
+  static_assert(BK * KVP <= L::BUF, "K is staged in one tile buffer");
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+
+  int bh, kt;
+  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, false, true, bh, kt);
+  const int b = bh / p.H, h = bh % p.H;
+  int start, len;
+  if (VARLEN) {
+    start = p.cu[b];
+    len = p.cu[b + 1] - start;
+  } else {
+    start = b * p.N;
+    len = p.N;
+  }
+  const int k0 = kt * BK;
+  if (k0 >= len) return;
+
+  const size_t stride = (size_t)p.H * D;
+  const size_t base = ((size_t)start * p.H + h) * D;
+  const u16* __restrict__ Qg = p.q + base;
+  const u16* __restrict__ dOg = p.dout + base;
+
+  const int wk0 = k0 + 32 * w;
+  const int kj = wk0 + lr;
+  const int kk = 32 * w + lr;  // this lane's key within the tile: its exchange row
+
+  KvState<D> st;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    st.dvT[bb] = f32x16{};
+    st.dkT[bb] = f32x16{};
+  }
+
+  const int qt_begin = CAUSAL ? k0 / BQ : 0;
+  const int n_qt = (len + BQ - 1) / BQ;
+
+  Dma tdma;
+  tdma.init(stride, w, lane);
+  auto bufp = [&](int qt) -> u16* { return lds + ((unsigned)(qt - qt_begin) % S) * L::BUF; };
+  u16* const xch = lds + XOFF;
+  auto e0 = [&](int qt) -> u16* { return xch + (qt & 1) * kXTile; };
+  auto e1 = [&](int qt) -> u16* { return xch + (2 + (qt & 1)) * kXTile; };
+  static_assert(BQ == 64 && kKvWaves == 4, "statistics copies assume 16 queries per wave");
+  auto issue = [&](int qt) {
+    u16* buf = bufp(qt);
+    const int q0 = qt * BQ;
+    tdma.issue(buf, Qg, q0, len, stride, w, lane);
+    tdma.issue(buf + L::TSZ, dOg, q0, len, stride, w, lane, false);
+#if __HIP_DEVICE_COMPILE__
+    const int qq = min(q0 + lane, len - 1);
+    const size_t si = stat_index<VARLEN>(p, b, h, start, qq);
+    if ((lane >> 4) == w) {
+      dma_lds_b32(p.mneg + si, buf + L::stat_pad(0, w) - 32 * w);
+      dma_lds_b32(p.dvec + si, buf + L::stat_pad(1, w) - 32 * w);
+    }
+#endif
+  };
+  constexpr int CNT = 2 * Dma::PER_WAVE + 2;
+
+  // Prologue: K rows through buffer 2, V rows through the exchange area, tiles qt_begin
+  // and qt_begin + 1 into buffers 0 and 1.
+  {
+    TileDma<BK, D, KVP, kKvWaves> kvdma;
+    kvdma.init(stride, w, lane);
+    kvdma.issue(lds + 2 * L::BUF, p.k + base, k0, len, stride, w, lane);
+    kvdma.issue(xch, p.v + base, k0, len, stride, w, lane);
+  }
+  issue(qt_begin);
+  if (qt_begin + 1 < n_qt) {
+    issue(qt_begin + 1);
+    wait_vmem_count<CNT>();
+  } else {
+    wait_vmem();
+  }
+  lds_barrier();
+  bf16x8 kq[8];  // K operands of the dQ product: head-dim column 32 w + lr, keys 16 s + ...
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e = (32 * w + lr) * KVP + 16 * s + 8 * g;
+    st.kf[s] = kj < len ? ld16(lds + 2 * L::BUF + e) : zero_bf16x8();
+    const bf16x8 v = kj < len ? ld16(xch + e) : zero_bf16x8();
+    st.vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    bf16x8 x = lds_tr_operand(lds + 2 * L::BUF, KVP, 16 * s, 32 * w, lane);
+    if (k0 + BK > len) {  // the staged rows past the end repeat row len - 1: zero those keys
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + 16 * s + 4 * g + (e & 3) + 8 * (e >> 2) >= len) x[e] = (__bf16)0.f;
+    }
+    kq[s] = to_agpr(x);
+  }
+  lds_barrier();
+  // Every wave clears its own rows of the four exchange tiles (the slots of the tiles
+  // before the first hold zeros, so the first dQ steps add nothing).
+  {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<u32x4_t*>(xch + x * kXTile + (32 * w) * kXq + 8 * (64 * i + lane)) = u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // dQ accumulator rows: query row n of this (sequence, head) is row stat_index(n). The
+  // two blocks whose atomics are pending start as zeros aimed at valid rows.
+  const uint32_t loff = (uint32_t)(4 * (4 * g * D + 32 * w + lr));
+  auto grow = [&](int q0) -> const char* {
+    return reinterpret_cast<const char*>(p.dqacc + stat_index<VARLEN>(p, b, h, start, max(q0, 0)) * D);
+  };
+  const XchLane xo = xch_lane_offsets(lane);
+  f32x16 qa = f32x16{}, qb = f32x16{};
+
+  KvBlock blk0, blk1;
+  bf16x8 rop[kKvPf], top[kKvPf], pb[2], db[2];
+  {
+    const u16* bf = bufp(qt_begin);
+#pragma unroll
+    for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 0, j, lane);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      kv_init_s<D>(blk0, bf, 0, r4, g);
+      kv_init_dp<D>(blk0, bf, 0, r4, g);
+    }
+    kv_phase_x<D, CAUSAL, true, false, false>(st, blk0, bf, 0, rop, blk1, pb, db, bf, 0, top, 0, kj, len, p.c, lane);
+#pragma unroll
+    for (int j = 0; j < kKvPf; ++j) rop[j] = kv_row_operand<D>(bf, 32, j, lane);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      kv_init_s<D>(blk1, bf, 32, r4, g);
+      kv_init_dp<D>(blk1, bf, 32, r4, g);
+    }
+  }
+  // (Keys past the end get finite -dS; their dQ terms vanish with the zeroed K operands,
+  // and their dK, dV rows are not stored.)
+  auto mask_of = [&](int q0) { return q0 + BQ > len || (CAUSAL && q0 < wk0 + 31); };
+
+  auto tile_step = [&](int qt) {
+    const u16* bc = bufp(qt);
+    const u16* bn = bufp(qt + 1);
+    const int q0 = qt * BQ;
+    const bool mask = mask_of(q0);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk1, bc, 32, rop, blk0, pb, db, bc, 0, top, q0, kj, len, p.c, lane);
+    xch_write(e0(qt), db, kk, g);
+    wait_vmem();  // tile qt + 1 (the only copies in flight) and the atomics of the last tile
+    lds_barrier();
+    if (qt + S - 1 < n_qt) issue(qt + S - 1);
+    fz_phase_y_atomics<D, true>(st, bc, 0, pb, db, top, bn, 0, rop, blk0, qa, grow(q0 - 96), qb, grow(q0 - 64),
+                                loff, lane);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk0, bn, 0, rop, blk1, pb, db, bc, 32, top, q0 + 32, kj, len, p.c, lane);
+    xch_write(e1(qt), db, kk, g);
+    fz_phase_y_dq<D, true>(st, bc, 32, pb, db, top, bn, 32, rop, blk1, e1(qt - 1), e0(qt), xo, kq, qa, qb, lane);
+  };
+  for (int qt = qt_begin; qt < n_qt - 1; ++qt) tile_step(qt);
+  {
+    const int qt = n_qt - 1;
+    const u16* bc = bufp(qt);
+    const int q0 = qt * BQ;
+    const bool mask = mask_of(q0);
+    kv_x<D, CAUSAL>(true, true, mask, st, blk1, bc, 32, rop, blk0, pb, db, bc, 0, top, q0, kj, len, p.c, lane);
+    xch_write(e0(qt), db, kk, g);
+    lds_barrier();
+    fz_phase_y_atomics<D, false>(st, bc, 0, pb, db, top, bc, 0, rop, blk0, qa, grow(q0 - 96), qb, grow(q0 - 64),
+                                 loff, lane);
+    kv_x<D, CAUSAL>(false, true, mask, st, blk0, bc, 0, rop, blk1, pb, db, bc, 32, top, q0 + 32, kj, len, p.c, lane);
+    xch_write(e1(qt), db, kk, g);
+    fz_phase_y_dq<D, false>(st, bc, 32, pb, db, top, bc, 32, rop, blk1, e1(qt - 1), e0(qt), xo, kq, qa, qb, lane);
+  }
+  const int ql = (n_qt - 1) * BQ;  // the last tile's first query
+
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    kv_acc_fence<D>(st.dvT[bb]);
+    kv_acc_fence<D>(st.dkT[bb]);
+  }
+  static_assert(kKvWaves * 64 * stage_pitch<D>() <= XOFF, "staging stays clear of the exchange tiles");
+  lds_barrier();
+  // The last block's dQ (its -dS was written after the last barrier of the loop).
+  f32x16 qc;
+  {
+    const u16* xl = e1(n_qt - 1);
+    bf16x8 xn = xch_operand(xl, xo, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a = xn;
+      if (s + 1 < 8) xn = xch_operand(xl, xo, s + 1);
+      if (s == 0)
+        dq_mfma_first(qc, a, kq[0]);
+      else
+        dq_mfma(qc, a, kq[s]);
+    }
+  }
+  u16* stg = lds + w * 64 * stage_pitch<D>();
+  stage_acc_rows<D>(stg, st.dkT, -p.scale, lr, g);
+  stage_acc_rows<D>(stg + 32 * stage_pitch<D>(), st.dvT, 1.f, lr, g);
+  agpr_acc_fence2(qa, qb);
+  agpr_acc_fence(qc);
+  {
+    const char* ga = grow(ql - 32);
+    const char* gb = grow(ql);
+    const char* gc = grow(ql + 32);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      atomic_add_f32(ga + dq_row_bytes<D>(r), loff, qa[r]);
+      atomic_add_f32(gb + dq_row_bytes<D>(r), loff, qb[r]);
+      atomic_add_f32(gc + dq_row_bytes<D>(r), loff, qc[r]);
+    }
+  }
+  const int valid = len - wk0;
+  store_staged_rows<D, 32>(stg, p.dk + base + (size_t)wk0 * stride, stride, valid, lane);
+  store_staged_rows<D, 32>(stg + 32 * stage_pitch<D>(), p.dv + base + (size_t)wk0 * stride, stride, valid, lane);
+}
+
+// dQ = -scale * (accumulator) as bf16 in the caller's layout, for 64 consecutive tokens
+// of one (sequence, head) per workgroup (a packed batch is one sequence of total_tokens);
+// 16 lanes per row, 8 values each: 512 contiguous bytes read and 256 written per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc, u16* __restrict__ dq,
+                                                             float mul, int H, int n_seq, int n_tiles) {
+  constexpr int LPR = D / 8, RPP = 256 / LPR, PASSES = kPreTokens / RPP;
+  const int h = blockIdx.x % H;
+  const int tile = (blockIdx.x / H) % n_tiles;
+  const int s = blockIdx.x / H / n_tiles;
+  const int n0 = tile * kPreTokens;
+  const int sub = threadIdx.x % LPR;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int n = n0 + ps * RPP + (int)threadIdx.x / LPR;
+    if (n < n_seq) {
+      const float* src = acc + (((size_t)s * H + h) * n_seq + n) * D + 8 * sub;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+      const f32x8 x = {a[0] * mul, a[1] * mul, a[2] * mul, a[3] * mul, c[0] * mul, c[1] * mul, c[2] * mul, c[3] * mul};
+      *reinterpret_cast<bf16x8*>(dq + (((size_t)s * n_seq + n) * H + h) * D + 8 * sub) = to_bf16x8(x);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------ bwd_dkdv, head_dim 64
@@ -1106,6 +1563,7 @@ BwdParams make_params(const Problem& pr) {
   p.mneg = pr.mneg;
   p.dvec_out = pr.dvec;
   p.mneg_out = pr.mneg;
+  p.dqacc = pr.dqacc;
   p.dq = static_cast<u16*>(pr.dq);
   p.dk = static_cast<u16*>(pr.dk);
   p.dv = static_cast<u16*>(pr.dv);
@@ -1128,7 +1586,8 @@ hipError_t launch_pre_t(const Problem& pr) {
   const int n_tiles = (n_seq + kPreTokens - 1) / kPreTokens;
   const dim3 grid((unsigned)((long long)n_tiles * n_seqs * pr.heads));
   hipLaunchKernelGGL((bwd_pre_kernel<D, T>), grid, dim3(256), 0, pr.stream, static_cast<const T*>(pr.o),
-                     static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg, pr.scale, pr.heads, n_seq, n_tiles);
+                     static_cast<const T*>(pr.dout), pr.lse, pr.dvec, pr.mneg, pr.dqacc, pr.scale, pr.heads, n_seq,
+                     n_tiles);
   return hipGetLastError();
 }
 
@@ -1141,6 +1600,30 @@ hipError_t launch_dkdv_t(const Problem& pr) {
     hipLaunchKernelGGL((bwd_dkdv_rows_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_fused_t(const Problem& pr) {
+  if constexpr (D != 128) {
+    return hipErrorInvalidValue;
+  } else {
+    BwdParams p = make_params(pr);
+    p.n_tiles = (pr.seqlen + kKvBK - 1) / kKvBK;
+    const dim3 grid((unsigned)(p.n_tiles * pr.batch * pr.heads));
+    hipLaunchKernelGGL((bwd_fused_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
+    return hipGetLastError();
+  }
+}
+
+template <int D>
+hipError_t launch_convert_t(const Problem& pr) {
+  const int n_seqs = pr.cu_seqlens ? 1 : pr.batch;
+  const int n_seq = pr.cu_seqlens ? pr.total_tokens : pr.seqlen;
+  const int n_tiles = (n_seq + kPreTokens - 1) / kPreTokens;
+  const dim3 grid((unsigned)((long long)n_tiles * n_seqs * pr.heads));
+  hipLaunchKernelGGL((bwd_dq_convert_kernel<D>), grid, dim3(256), 0, pr.stream, pr.dqacc, static_cast<u16*>(pr.dq),
+                     -pr.scale, pr.heads, n_seq, n_tiles);
   return hipGetLastError();
 }
 
@@ -1172,5 +1655,14 @@ hipError_t launch_bwd_dkdv_bf16(const Problem& p) { FA_DISPATCH(launch_dkdv_t, p
 hipError_t launch_bwd_dq_bf16(const Problem& p) { FA_DISPATCH(launch_dq_t, p); }
 
 hipError_t launch_bwd_dq_stats_bf16(const Problem& p) { FA_DISPATCH(launch_dq_stats_t, p); }
+
+hipError_t launch_bwd_fused_bf16(const Problem& p) {
+  if (p.head_dim != 128) return hipErrorInvalidValue;
+  FA_DISPATCH(launch_fused_t, p);
+}
+
+hipError_t launch_bwd_dq_convert(const Problem& p) {
+  return p.head_dim == 64 ? launch_convert_t<64>(p) : launch_convert_t<128>(p);
+}
 
 }  // namespace fa

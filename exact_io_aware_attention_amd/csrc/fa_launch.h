@@ -21,6 +21,8 @@ struct Problem {
   void* dv;
   float* dvec;         // backward workspace: D_i = rowsum(dO * O), same layout as lse
   float* mneg;         // backward workspace: -LSE_i / scale, same layout as lse
+  float* dqacc;        // fused backward workspace: fp32 dQ accumulator (lse rows + 64) x head_dim,
+                       // zeroed by launch_bwd_pre when set
   const int32_t* cu_seqlens;  // NULL: padded batch
   int batch, heads, seqlen, head_dim;
   int total_tokens;    // batch * seqlen, or the packed token count
@@ -37,6 +39,10 @@ hipError_t launch_bwd_dkdv_bf16(const Problem& p);
 hipError_t launch_bwd_dq_bf16(const Problem& p);
 // The dQ pass that also writes the row statistics (p.dvec, p.mneg) from p.o, p.dout, p.lse.
 hipError_t launch_bwd_dq_stats_bf16(const Problem& p);
+// The fused backward (head_dim 128, bf16): dK, dV, and dQ added into p.dqacc by fp32
+// atomics; then the conversion dq = -scale * dqacc.
+hipError_t launch_bwd_fused_bf16(const Problem& p);
+hipError_t launch_bwd_dq_convert(const Problem& p);
 hipError_t launch_bwd_dkdv_fp32(const Problem& p);
 hipError_t launch_bwd_dq_fp32(const Problem& p);
 

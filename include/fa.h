@@ -122,6 +122,33 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int dtype, void* stream);
 
 /*
+ * The backward in one pass over the key tiles (head_dim 128, FA_DTYPE_BF16): the same
+ * arguments, outputs and tolerances as fa_bwd, with dQ accumulated by fp32 atomics from
+ * the dK/dV kernel instead of a separate dQ pass. Recomputing P by blocks ("Recalcular
+ * en vez de guardar", AI Atlas summary) then costs five matrix products per tile instead
+ * of seven. Three kernels run on `stream`, in order: the row statistics (which also clear
+ * the accumulator), the fused dK/dV/dQ kernel, and the conversion of the accumulator to
+ * dq. dk and dv are bitwise reproducible; dq depends on the order in which the atomics
+ * land, so it may differ from run to run in its last bits (the pages' "exact and
+ * deterministic", "Desempenho e eficiência": fa_bwd keeps that; this entry point trades
+ * the last bits of dq for speed).
+ * workspace: at least fa_bwd_atomic_workspace_bytes(...) bytes (fa_bwd's statistics, then
+ * an fp32 accumulator of (heads * tokens + 64) x head_dim), 256-byte aligned, owned by
+ * the caller; its contents on entry do not matter. Other head_dim or dtype values return
+ * FA_ERR_UNSUPPORTED; fa_bwd covers them.
+ */
+size_t fa_bwd_atomic_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
+                                     int varlen, int total_tokens);
+int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes,
+                  int batch, int heads, int seqlen, int head_dim,
+                  float softmax_scale, int causal,
+                  const int32_t* cu_seqlens, int total_tokens,
+                  int dtype, void* stream);
+
+/*
  * fa_bwd for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same arguments without the
  * workspace, the same kernels and results. The row statistics go to a fixed device array

@@ -34,8 +34,8 @@ def declared_functions(headers=(HEADER,)):
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_bwd_noalloc",
-                                    "fa_bwd_preprocess",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes", "fa_bwd_dkdv",
+                                    "fa_bwd_dq", "fa_bwd_dq_stats", "fa_bwd_noalloc", "fa_bwd_preprocess",
                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
                                     "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_strerror"]
 
@@ -156,6 +156,45 @@ def test_stage_argument_checks():
                               **sc, **common) == fa.FA_ERR_WORKSPACE
     assert fa.fa_bwd_dq_stats(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, **ws, softmax_scale=-1.0, causal=0,
                               **common) == fa.FA_ERR_INVALID_ARG
+
+
+def _atomic(**kw):
+    args = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, workspace=A, workspace_bytes=1 << 30,
+                batch=1, heads=2, seqlen=16, head_dim=128, softmax_scale=0.125, causal=1, cu_seqlens=None,
+                total_tokens=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd_atomic(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),          # the fused kernel is built for 128
+    (dict(dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=A + 16), fa.FA_ERR_WORKSPACE),
+    # room for fa_bwd's statistics but not for the accumulator
+    (dict(workspace_bytes=2 * 256), fa.FA_ERR_WORKSPACE),
+    (dict(cu_seqlens=A, total_tokens=0), fa.FA_OK),
+])
+def test_atomic_bwd_argument_checks(kw, code):
+    _lib()
+    assert _atomic(**kw) == code
+
+
+def test_atomic_workspace_size():
+    _lib()
+    # fa_bwd's statistics, then (heads * tokens + 64) rows of head_dim fp32
+    assert fa.fa_bwd_atomic_workspace_bytes(4, 32, 4096, 128, 0, 0) == (
+        2 * 4 * 32 * 4096 * 4 + (32 * 4 * 4096 + 64) * 128 * 4)
+    assert fa.fa_bwd_atomic_workspace_bytes(1, 2, 16, 128, 0, 0) == 2 * 256 + (2 * 16 + 64) * 128 * 4
+    assert fa.fa_bwd_atomic_workspace_bytes(7, 32, 2048, 128, 1, 16384) == (
+        2 * 32 * 16384 * 4 + (32 * 16384 + 64) * 128 * 4)
+    assert fa.fa_bwd_atomic_workspace_bytes(1, 1, 1, 80, 0, 0) == 0
+    assert _atomic(workspace_bytes=fa.fa_bwd_atomic_workspace_bytes(1, 2, 16, 128, 0, 0) - 4) == fa.FA_ERR_WORKSPACE
 
 
 def test_workspace_size():
