@@ -295,7 +295,9 @@ def ceilings(reps: int = 5):
     clock as the HIP runtime reports them (the dense bf16 MFMA peak follows as CUs x 4096
     FLOP/clk x clock), then three loops timed with HIP events on the launch stream (median
     of `reps`): independent bf16 MFMA chains in every SIMD, independent v_exp_f32 and fp32
-    FMA chains in every lane (the vector-ALU roof of the softmax), and a 1 GiB copy."""
+    FMA chains in every lane (the vector-ALU roof of the softmax), LDS operand reads, one
+    MFMA chain per wave with vector work between its MFMAs (how much of it the matrix pipe
+    hides), and a 1 GiB copy."""
     import torch
     import exact_io_aware_attention_amd as fa
     info = fa.fa_device_info(torch.cuda.current_device())
@@ -319,22 +321,34 @@ def ceilings(reps: int = 5):
         if st != fa.FA_OK:
             raise fa.FAError(st, name)
 
-    mblocks, miters = 4 * cus, 400          # four waves per SIMD, four chains per wave
+    mblocks, miters = 4 * cus, 2000         # four waves per SIMD, four chains per wave, ~1 ms
     vblocks, viters = 32 * cus, 1000
     out = torch.empty(max(mblocks, vblocks) * 256, device="cuda", dtype=torch.float32)
     t_mfma = timed(lambda: ok(fa.fa_ubench_mfma_bf16(out.data_ptr(), mblocks, miters, sp), "mfma"))
     t_exp = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 0, sp), "exp"))
     t_fma = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 1, sp), "fma"))
-    lblocks, liters = 4 * cus, 1000          # four waves per SIMD
+    lblocks, liters = 2 * cus, 4000          # two 64 KiB workgroups per CU (two waves per SIMD)
     t_ldsr = timed(lambda: ok(fa.fa_ubench_lds(out.data_ptr(), lblocks, liters, 0, sp), "lds rows"))
     t_ldst = timed(lambda: ok(fa.fa_ubench_lds(out.data_ptr(), lblocks, liters, 1, sp), "lds transposed"))
+    # One dependent MFMA chain per wave with n independent vector operations after each
+    # MFMA: cycles per MFMA (at the reported clock) at one and two waves per SIMD, with the
+    # accumulator in VGPRs or AGPRs; 32 cycles is the matrix pipe's rate.
+    citers = 2000
+    coexec = {}
+    for wps in (1, 2):
+        for nv, op in ((0, 1), (4, 1), (8, 1), (2, 0), (4, 0)):
+            for ag in (0, 1):
+                t = timed(lambda: ok(fa.fa_ubench_mfma_valu(out.data_ptr(), wps * cus, citers, nv, ag, op, sp),
+                                     "mfma+valu"))
+                key = f"{wps}w_{'exp' if op == 0 else 'fma'}{nv}_{'agpr' if ag else 'vgpr'}"
+                coexec[key] = round(t * 1e-3 * clk_khz * 1e3 / (wps * citers * 4), 1)
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
     dst = torch.empty_like(src)
     t_copy = timed(lambda: ok(fa.fa_ubench_copy(src.data_ptr(), dst.data_ptr(), nbytes, 16 * cus, sp), "copy"))
     del src, dst, out
     torch.cuda.empty_cache()
-    mfma_flops = mblocks * 4 * miters * 4 * 32768.0
+    mfma_flops = mblocks * 4 * miters * 8 * 32768.0
     lane_ops = vblocks * 256 * viters * 8.0
     clk_hz = clk_khz * 1e3
     return {
@@ -353,6 +367,7 @@ def ceilings(reps: int = 5):
         "lds_tr_operands_per_clk_cu": round(lblocks * 4 * liters * 8 / (t_ldst * 1e-3) / clk_hz / cus, 4),
         "lds_row_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldsr * 1e-3) / 1e12, 1),
         "lds_tr_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldst * 1e-3) / 1e12, 1),
+        "mfma_chain_cycles_per_mfma": coexec,
         "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
                "lds_rows": round(t_ldsr, 4), "lds_tr": round(t_ldst, 4)},
         "note": "rates per clock use the reported maximum clock; the clock under load may be lower",

@@ -1,7 +1,7 @@
 // fa_ubench.hip - device facts and ceiling measurements for the roofline of the attention
-// kernels: the compute-unit count and clock the device reports, and three loops that
-// measure what the chip sustains (bf16 MFMA throughput, vector-ALU exponential and FMA
-// rates, HBM copy bandwidth). Declarations: include/fa_ubench.h.
+// kernels: the compute-unit count and clock the device reports, and loops that measure
+// what the chip sustains (bf16 MFMA throughput, vector-ALU exponential and FMA rates, LDS
+// operand reads, HBM copy bandwidth). Declarations: include/fa_ubench.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -14,9 +14,9 @@ namespace {
 
 constexpr int kUbThreads = 256;
 
-// Four independent 32x32x16 bf16 MFMA chains per wave: the matrix pipe never waits for
-// a result, so the loop runs at the pipe's issue rate. The operands depend on the lane
-// so nothing folds; the accumulators are summed into `out` at the end.
+// Four independent 32x32x16 bf16 MFMA chains per wave, two rounds per step (8 MFMAs): the
+// matrix pipe never waits for a result, so the loop runs at the pipe's issue rate. The
+// operands depend on the lane so nothing folds; the accumulators are summed into `out`.
 __global__ __launch_bounds__(kUbThreads) void ub_mfma_kernel(float* __restrict__ out, int iters) {
   const int tid = threadIdx.x;
   const u32x4 bits = {0x3f803f80u ^ (uint32_t)tid, 0x3f003f00u, 0x3e803e80u, 0x3f403f40u ^ (uint32_t)blockIdx.x};
@@ -24,15 +24,75 @@ __global__ __launch_bounds__(kUbThreads) void ub_mfma_kernel(float* __restrict__
   const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{bits[3], bits[2], bits[1], bits[0]});
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int i = 0; i < iters; ++i) {
-    c0 = mfma32(a, b, c0);
-    c1 = mfma32(b, a, c1);
-    c2 = mfma32(a, a, c2);
-    c3 = mfma32(b, b, c3);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      c0 = mfma32(a, b, c0);
+      c1 = mfma32(b, a, c1);
+      c2 = mfma32(a, a, c2);
+      c3 = mfma32(b, b, c3);
+    }
   }
   float s = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
   out[(size_t)blockIdx.x * kUbThreads + tid] = s;
+}
+
+// One dependent MFMA chain per wave with NV independent vector operations after each MFMA
+// (in eight chains of their own: fp32 FMAs, or exponentials when EXP), the MFMA's
+// accumulator in VGPRs (the compiler's form) or in AGPRs (inline asm, as the attention
+// kernels pin their output accumulators): how much vector work hides under the matrix
+// pipe at a given occupancy, which is what the attention kernels' softmax needs.
+template <int NV, bool AGPR, bool EXP>
+__global__ __launch_bounds__(kUbThreads) void ub_coexec_kernel(float* __restrict__ out, int iters) {
+  const int tid = threadIdx.x;
+  const u32x4 bits = {0x3f803f80u ^ (uint32_t)tid, 0x3f003f00u, 0x3e803e80u, 0x3f403f40u ^ (uint32_t)blockIdx.x};
+  const bf16x8 a = __builtin_bit_cast(bf16x8, bits);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{bits[3], bits[2], bits[1], bits[0]});
+  f32x16 c = f32x16{};
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = 0.25f + 0.01f * k + 1e-4f * (tid & 63);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (AGPR)
+        mfma32_agpr(c, a, b);
+      else
+        c = mfma32(a, b, c);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if constexpr (EXP)
+          x[k & 7] = __builtin_amdgcn_exp2f(-x[k & 7]);
+        else
+          x[k & 7] = fmaf(x[k & 7], 0.999f, 1e-3f);
+      }
+      step_fence();
+    }
+  }
+  if constexpr (AGPR) agpr_acc_fence(c);
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c[r];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += x[k];
+  out[(size_t)blockIdx.x * kUbThreads + tid] = s;
+}
+
+template <int NV>
+hipError_t launch_coexec(float* out, int blocks, int iters, bool agpr, bool ex, hipStream_t st) {
+  if (agpr) {
+    if (ex)
+      hipLaunchKernelGGL((ub_coexec_kernel<NV, true, true>), dim3(blocks), dim3(kUbThreads), 0, st, out, iters);
+    else
+      hipLaunchKernelGGL((ub_coexec_kernel<NV, true, false>), dim3(blocks), dim3(kUbThreads), 0, st, out, iters);
+  } else {
+    if (ex)
+      hipLaunchKernelGGL((ub_coexec_kernel<NV, false, true>), dim3(blocks), dim3(kUbThreads), 0, st, out, iters);
+    else
+      hipLaunchKernelGGL((ub_coexec_kernel<NV, false, false>), dim3(blocks), dim3(kUbThreads), 0, st, out, iters);
+  }
+  return hipGetLastError();
 }
 
 // Eight independent chains per lane of one vector operation: op 0 the exponential the
@@ -58,11 +118,13 @@ __global__ __launch_bounds__(kUbThreads) void ub_valu_kernel(float* __restrict__
   out[(size_t)blockIdx.x * kUbThreads + tid] = s;
 }
 
-// LDS operand reads as the attention kernels issue them, eight per step in every wave:
-// op 0 row-wise 16-byte reads (ds_read_b128: lane l reads row l % 32, chunk l / 32, of a
-// tile with a 68-dword pitch, conflict-free), op 1 transpose reads (ds_read_b64_tr_b16 in
-// the operand pattern of lds_tr_operand on a tile with an 80-dword pitch). The rows read
-// move by 16 each step so the loads stay in the loop; their bits are folded into `out`.
+// LDS operand reads as the attention kernels issue them: eight 1 KiB operands per step in
+// every wave, all eight in flight before their values are consumed (by an empty asm use:
+// no arithmetic), at constant offsets from a base that alternates between the two halves
+// of the tile each step (one address add, and the loads stay in the loop). op 0: row-wise
+// reads of a swizzled 64-row tile (swz_row_operand, one ds_read_b128 per operand); op 1:
+// transpose reads of the same tile (swz_tr_operand, two ds_read_b64_tr_b16 per operand).
+// The first dword of each step's first operand is folded into `out`.
 constexpr int kUbLdsElems = 32768;  // 64 KiB of bf16
 
 __global__ __launch_bounds__(kUbThreads) void ub_lds_kernel(float* __restrict__ out, int iters, int op) {
@@ -70,25 +132,25 @@ __global__ __launch_bounds__(kUbThreads) void ub_lds_kernel(float* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63;
   for (int i = tid; i < kUbLdsElems; i += kUbThreads) lds[i] = (u16)(i * 2654435761u >> 16);
   __syncthreads();
+  constexpr int HALF = 64 * swz_pitch<128>();  // one 64-row tile
   uint32_t acc = 0;
+  bf16x8 x[8];
   if (op == 0) {
-    constexpr int P = 136;  // pitch_rows<128>()
-    const u16* base = lds + (lane & 31) * P + 8 * (lane >> 5);
-    for (int i = 0; i < iters; ++i)
+    for (int i = 0; i < iters; ++i) {
+      const u16* t = lds + (i & 1) * HALF;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (((i * 3 + j) & 7) * 16) * P + 16 * (j & 3));
-        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
-      }
+      for (int j = 0; j < 8; ++j) x[j] = swz_row_operand<128>(t, 32 * (j & 1), j >> 1, lane);
+      asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+      acc ^= __builtin_bit_cast(u32x4, x[0])[0];
+    }
   } else {
-    constexpr int P = 160;  // pitch_tr<128>()
-    for (int i = 0; i < iters; ++i)
+    for (int i = 0; i < iters; ++i) {
+      const u16* t = lds + (i & 1) * HALF;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 v = lds_tr_operand(lds, P, ((i * 3 + j) & 7) * 16, 32 * (j & 3), lane);
-        const u32x4 u = __builtin_bit_cast(u32x4, v);
-        acc ^= u[0] ^ u[1] ^ u[2] ^ u[3];
-      }
+      for (int j = 0; j < 8; ++j) x[j] = swz_tr_operand<128>(t, 16 * (j & 3), 32 * (j >> 2), lane);
+      asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+      acc ^= __builtin_bit_cast(u32x4, x[0])[0];
+    }
   }
   out[(size_t)blockIdx.x * kUbThreads + tid] = __uint_as_float(acc);
 }
@@ -141,6 +203,21 @@ FA_EXPORT int fa_ubench_lds(float* out, int blocks, int iters, int op, void* str
   hipLaunchKernelGGL(fa::ub_lds_kernel, dim3(blocks), dim3(fa::kUbThreads), 0, static_cast<hipStream_t>(stream),
                      out, iters, op);
   return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
+}
+
+FA_EXPORT int fa_ubench_mfma_valu(float* out, int blocks, int iters, int nvalu, int agpr, int op, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || (agpr != 0 && agpr != 1) || (op != 0 && op != 1)) return FA_UB_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool ag = agpr == 1, ex = op == 0;
+  hipError_t e;
+  switch (nvalu) {
+    case 0: e = fa::launch_coexec<0>(out, blocks, iters, ag, ex, st); break;
+    case 2: e = fa::launch_coexec<2>(out, blocks, iters, ag, ex, st); break;
+    case 4: e = fa::launch_coexec<4>(out, blocks, iters, ag, ex, st); break;
+    case 8: e = fa::launch_coexec<8>(out, blocks, iters, ag, ex, st); break;
+    default: return FA_UB_ERR_INVALID_ARG;
+  }
+  return e == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
 }
 
 FA_EXPORT int fa_ubench_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {

@@ -31,8 +31,8 @@ enum { FA_UB_OK = 0, FA_UB_ERR_INVALID_ARG = 1, FA_UB_ERR_HIP = 4 };
 int fa_device_info(int device, int* compute_units, int* max_clock_khz, int* l2_bytes, char* arch,
                    int arch_len);
 
-/* `blocks` workgroups of four waves; each wave issues 4 * iters independent
- * v_mfma_f32_32x32x16_bf16 (32768 FLOP each). out: blocks * 256 floats (written). */
+/* `blocks` workgroups of four waves; each wave issues 8 * iters v_mfma_f32_32x32x16_bf16
+ * (32768 FLOP each) in four independent chains. out: blocks * 256 floats (written). */
 int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* stream);
 
 /* `blocks` workgroups of 256 lanes; each lane runs 8 * iters vector operations in eight
@@ -40,11 +40,20 @@ int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* stream);
  * out: blocks * 256 floats (written). */
 int fa_ubench_valu(float* out, int blocks, int iters, int op, void* stream);
 
-/* `blocks` workgroups of four waves, each with a 64 KiB LDS tile; every wave issues
- * 8 * iters LDS operand reads in the forms the attention kernels use: op 0 row-wise
- * ds_read_b128 (1 KiB per wave instruction), op 1 transpose reads ds_read_b64_tr_b16
- * (512 B). Bank-conflict-free addressing. out: blocks * 256 floats (written). */
+/* `blocks` workgroups of four waves, each with a 64 KiB LDS tile; every wave reads
+ * 8 * iters operands of 1 KiB (32 x 16 bf16) in the forms the attention kernels use,
+ * eight in flight at a time: op 0 row-wise (one ds_read_b128 each), op 1 transposed (two
+ * ds_read_b64_tr_b16 each), from a swizzled tile without bank conflicts.
+ * out: blocks * 256 floats (written). */
 int fa_ubench_lds(float* out, int blocks, int iters, int op, void* stream);
+
+/* `blocks` workgroups of four waves; each wave runs one dependent chain of 4 * iters
+ * v_mfma_f32_32x32x16_bf16 with nvalu (0, 2, 4 or 8) independent vector operations after
+ * each MFMA: op 0 the exponential v_exp_f32, op 1 an fp32 FMA. agpr 1 keeps the MFMA's
+ * accumulator in AGPRs, 0 in VGPRs. The time per MFMA at one or two workgroups per SIMD
+ * (blocks = 1 or 2 per SIMD) measures how much vector work the matrix pipe hides.
+ * out: blocks * 256 floats (written). */
+int fa_ubench_mfma_valu(float* out, int blocks, int iters, int nvalu, int agpr, int op, void* stream);
 
 /* Copies `bytes` (a multiple of 16; src and dst 16-byte aligned, not overlapping) from
  * src to dst with `blocks` workgroups of 256 lanes, 16 bytes per lane per access. */
