@@ -141,6 +141,7 @@ __device__ __forceinline__ void f8_tile(F8State<D>& st, const uint8_t* Ks, const
   }
   const float nb = st.m_ref == -INFINITY ? 0.f : -st.m_ref * c;
   i32x8 pf;
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: no chain of 32 dependent adds
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -149,13 +150,15 @@ __device__ __forceinline__ void f8_tile(F8State<D>& st, const uint8_t* Ks, const
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         e[u] = fast_exp2(fmaf(s[j][r + u], c, nb));  // exp2(-inf) = 0 for masked keys
-        st.l_run += e[u];
+        ls[u] += e[u];
       }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      // the low word's old value is e[0]'s own register (both halves are written)
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], __float_as_int(e[0]), false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
       pf[4 * j + r / 4] = w;  // bytes 16 j + r .. + 3
     }
   }
+  st.l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
   for (int mt = 0; mt < NM; ++mt) st.oacc[mt] = mfma_fp8(f8_vt_operand(Vs, mt, lane), pf, st.oacc[mt]);
 }
