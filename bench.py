@@ -169,9 +169,38 @@ def standard_attention(q, k, v, do, scale: float, causal: bool, reps: int = 3):
             "nxn_bytes_per_step": nxn, "passes": reps + 1}, o.permute(0, 2, 1, 3)
 
 
+def time_calls(call, reps: int = 20, rounds: int = 5):
+    """Two timings of a library call on the current stream (HIP events): the steady-state
+    time per call, as the median over `rounds` of `reps` back-to-back calls (the way the
+    step is timed), and the median time of a single call that starts on an idle GPU (what
+    a lone call waits, launch and ramp-up included)."""
+    import torch
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    batch = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        batch.append(e0.elapsed_time(e1) / reps)
+    single = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1))
+    return sorted(batch)[len(batch) // 2], sorted(single)[len(single) // 2]
+
+
 def decode_bench(reps: int = 20):
-    """fa_fwd_decode on the decode workloads: median time of `reps` calls (HIP events on
-    the launch stream) and the achieved rate of the algorithmic bytes (K and V read
+    """fa_fwd_decode on the decode workloads: the steady-state time per call (and a lone
+    call's, see time_calls) and the achieved rate of the algorithmic bytes (K and V read
     once, Q read, O and LSE written) against the HBM peak."""
     import torch
     import exact_io_aware_attention_amd as fa
@@ -193,21 +222,12 @@ def decode_bench(reps: int = 20):
             if st != fa.FA_OK:
                 raise fa.FAError(st, "fa_fwd_decode")
 
-        for _ in range(3):
-            call()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            call()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = sorted(ts)[len(ts) // 2]
+        ms, ms_single = time_calls(call, reps)
         algo = 2 * B * Nk * H * d * 2 + 2 * B * Nq * H * d * 2 + B * H * Nq * 4
         gbs = algo / (ms * 1e-3) / 1e9
         res[name] = {"workload": w.description, "batch": B, "heads": H, "seqlen_q": Nq, "seqlen_k": Nk,
-                     "head_dim": d, "causal": w.causal, "ms": round(ms, 4), "algorithmic_bytes": algo,
+                     "head_dim": d, "causal": w.causal, "ms": round(ms, 4), "ms_single_call": round(ms_single, 4),
+                     "algorithmic_bytes": algo,
                      "achieved_gbs": round(gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS,
                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm"}
         del q, k, v, o, lse, ws
@@ -215,9 +235,9 @@ def decode_bench(reps: int = 20):
 
 
 def fp8_bench(reps: int = 20, batch=None, seqlen=None):
-    """fa_fwd_fp8 on the 8-bit workloads: median time of `reps` calls (HIP events on the
-    launch stream) and the forward's algorithmic FLOPs (2 GEMM units, halved under causal)
-    per second against the fp8 MFMA peak."""
+    """fa_fwd_fp8 on the 8-bit workloads: the steady-state time per call (and a lone
+    call's, see time_calls) and the forward's algorithmic FLOPs (2 GEMM units, halved
+    under causal) per second against the fp8 MFMA peak."""
     import torch
     import exact_io_aware_attention_amd as fa
     import workloads as W
@@ -235,22 +255,13 @@ def fp8_bench(reps: int = 20, batch=None, seqlen=None):
             if st != fa.FA_OK:
                 raise fa.FAError(st, "fa_fwd_fp8")
 
-        for _ in range(3):
-            call()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            call()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = sorted(ts)[len(ts) // 2]
+        ms, ms_single = time_calls(call, reps)
         flops = 2 * (2.0 * B * H * N * N * d) * (0.5 if w.causal else 1.0)
         tf = flops / (ms * 1e-3) / 1e12
         res[name] = {"workload": w.description + (" (resized)" if batch or seqlen else ""),
                      "batch": B, "heads": H, "seqlen": N, "head_dim": d,
-                     "causal": w.causal, "ms": round(ms, 4), "tflops": round(tf, 2), "bound": "mfma",
+                     "causal": w.causal, "ms": round(ms, 4), "ms_single_call": round(ms_single, 4),
+                     "tflops": round(tf, 2), "bound": "mfma",
                      "peak_tflops": PEAK_FP8_TFLOPS, "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
         del q8, k8, v8, o, lse
     return res
