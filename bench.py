@@ -307,7 +307,8 @@ def ceilings(reps: int = 5):
     of `reps`): independent bf16 MFMA chains in every SIMD, independent v_exp_f32 and fp32
     FMA chains in every lane (the vector-ALU roof of the softmax), LDS operand reads, one
     MFMA chain per wave with vector work between its MFMAs (how much of it the matrix pipe
-    hides), and a 1 GiB copy."""
+    hides), independent MFMA chains with the forward's vector mix per MFMA (the MFMA rate
+    that mix allows at one and two waves per SIMD), and a 1 GiB copy."""
     import torch
     import exact_io_aware_attention_amd as fa
     info = fa.fa_device_info(torch.cuda.current_device())
@@ -352,6 +353,17 @@ def ceilings(reps: int = 5):
                                      "mfma+valu"))
                 key = f"{wps}w_{'exp' if op == 0 else 'fma'}{nv}_{'agpr' if ag else 'vgpr'}"
                 coexec[key] = round(t * 1e-3 * clk_khz * 1e3 / (wps * citers * 4), 1)
+    # The forward's instruction mix (one exponential and three FMAs per MFMA) without its
+    # dependences, LDS reads or barriers, four independent MFMA chains per wave, at one and
+    # two waves per SIMD: the share of the MFMA peak that mix allows, beside the MFMAs alone.
+    xiters = 4000
+    mix = {}
+    for wps in (1, 2):
+        for m in (0, 1):
+            t = timed(lambda: ok(fa.fa_ubench_mfma_mix(out.data_ptr(), wps * cus, xiters, m, sp), "mfma mix"))
+            fl = wps * cus * 4 * xiters * 4 * 32768.0
+            mix[f"{wps}w_{'softmax_mix' if m else 'mfma_only'}_frac_of_peak"] = round(
+                fl / (t * 1e-3) / (cus * BF16_FLOP_PER_CLK_CU * clk_khz * 1e3), 3)
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
     dst = torch.empty_like(src)
@@ -378,6 +390,7 @@ def ceilings(reps: int = 5):
         "lds_row_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldsr * 1e-3) / 1e12, 1),
         "lds_tr_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldst * 1e-3) / 1e12, 1),
         "mfma_chain_cycles_per_mfma": coexec,
+        "mfma_with_forward_mix": mix,
         "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
                "lds_rows": round(t_ldsr, 4), "lds_tr": round(t_ldst, 4)},
         "note": "rates per clock use the reported maximum clock; the clock under load may be lower",

@@ -27,7 +27,7 @@ __all__ = [
     "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
     "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_lds", "fa_ubench_copy",
-    "fa_ubench_mfma_valu",
+    "fa_ubench_mfma_valu", "fa_ubench_mfma_mix",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
@@ -103,6 +103,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_ubench_copy.restype = i32
     lib.fa_ubench_mfma_valu.argtypes = [vp, i32, i32, i32, i32, i32, vp]
     lib.fa_ubench_mfma_valu.restype = i32
+    lib.fa_ubench_mfma_mix.argtypes = [vp, i32, i32, i32, vp]
+    lib.fa_ubench_mfma_mix.restype = i32
     _LIB = lib
     return lib
 
@@ -240,6 +242,10 @@ def fa_ubench_copy(src: int, dst: int, nbytes: int, blocks: int, stream: Optiona
 def fa_ubench_mfma_valu(out: int, blocks: int, iters: int, nvalu: int, agpr: int, op: int,
                         stream: Optional[int]) -> int:
     return load_library().fa_ubench_mfma_valu(out, blocks, iters, nvalu, agpr, op, stream)
+
+
+def fa_ubench_mfma_mix(out: int, blocks: int, iters: int, mix: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_mfma_mix(out, blocks, iters, mix, stream)
 
 
 # ---------------------------------------------------------------- torch marshalling

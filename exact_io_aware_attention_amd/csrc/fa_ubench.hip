@@ -95,6 +95,48 @@ hipError_t launch_coexec(float* out, int blocks, int iters, bool agpr, bool ex, 
   return hipGetLastError();
 }
 
+// The forward's mix of work with none of its dependences: per wave, four independent
+// 32x32x16 bf16 MFMA chains, and with MIX after every MFMA one exponential and three FMAs
+// on independent vector chains (the forward issues about one exponential and three other
+// vector instructions per MFMA), each MFMA and its vector work closed by a scheduling
+// barrier as in the kernels. No LDS, no copies, no barriers, no data flow from the MFMAs
+// to the vector work: the MFMA rate this reaches at one or two workgroups per SIMD bounds
+// what a schedule of the forward's instruction mix can reach.
+template <bool MIX>
+__global__ __launch_bounds__(kUbThreads) void ub_mix_kernel(float* __restrict__ out, int iters) {
+  const int tid = threadIdx.x;
+  const u32x4 bits = {0x3f803f80u ^ (uint32_t)tid, 0x3f003f00u, 0x3e803e80u, 0x3f403f40u ^ (uint32_t)blockIdx.x};
+  const bf16x8 a = __builtin_bit_cast(bf16x8, bits);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{bits[3], bits[2], bits[1], bits[0]});
+  float x[8], y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[k] = 0.25f + 0.01f * k + 1e-4f * (tid & 63);
+    y[k] = x[k];
+  }
+  f32x16 c[4] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      c[m] = mfma32(a, b, c[m]);
+      if constexpr (MIX) {
+        x[(2 * m) & 7] = __builtin_amdgcn_exp2f(-x[(2 * m) & 7]);
+#pragma unroll
+        for (int f = 0; f < 3; ++f) y[(3 * m + f) & 7] = fmaf(y[(3 * m + f) & 7], 0.999f, 1e-3f);
+      }
+      step_fence();
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[m][r];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += x[k] + y[k];
+  out[(size_t)blockIdx.x * kUbThreads + tid] = s;
+}
+
 // Eight independent chains per lane of one vector operation: op 0 the exponential the
 // attention kernels use (v_exp_f32, x <- 2^-x stays in (0, 1]), op 1 an fp32 FMA.
 __global__ __launch_bounds__(kUbThreads) void ub_valu_kernel(float* __restrict__ out, int iters, int op) {
@@ -218,6 +260,16 @@ FA_EXPORT int fa_ubench_mfma_valu(float* out, int blocks, int iters, int nvalu, 
     default: return FA_UB_ERR_INVALID_ARG;
   }
   return e == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
+}
+
+FA_EXPORT int fa_ubench_mfma_mix(float* out, int blocks, int iters, int mix, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || (mix != 0 && mix != 1)) return FA_UB_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mix)
+    hipLaunchKernelGGL(fa::ub_mix_kernel<true>, dim3(blocks), dim3(fa::kUbThreads), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL(fa::ub_mix_kernel<false>, dim3(blocks), dim3(fa::kUbThreads), 0, st, out, iters);
+  return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
 }
 
 FA_EXPORT int fa_ubench_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {

@@ -55,6 +55,14 @@ int fa_ubench_lds(float* out, int blocks, int iters, int op, void* stream);
  * out: blocks * 256 floats (written). */
 int fa_ubench_mfma_valu(float* out, int blocks, int iters, int nvalu, int agpr, int op, void* stream);
 
+/* `blocks` workgroups of four waves; each wave issues 4 * iters v_mfma_f32_32x32x16_bf16
+ * in four independent chains. With mix 1, every MFMA is followed by one v_exp_f32 and
+ * three fp32 FMAs on independent vector chains (the forward's instruction mix per MFMA,
+ * without its dependences, LDS reads, copies or barriers); mix 0 issues the MFMAs alone.
+ * At blocks = 1 or 2 per SIMD the MFMA rate bounds what a schedule of that mix can reach
+ * at that occupancy. out: blocks * 256 floats (written). */
+int fa_ubench_mfma_mix(float* out, int blocks, int iters, int mix, void* stream);
+
 /* Copies `bytes` (a multiple of 16; src and dst 16-byte aligned, not overlapping) from
  * src to dst with `blocks` workgroups of 256 lanes, 16 bytes per lane per access. */
 int fa_ubench_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);

@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
 
 def test_measurement_header_declares_its_calls():
     assert declared_functions([os.path.join(ROOT, "include", "fa_ubench.h")]) == [
-        "fa_device_info", "fa_ubench_copy", "fa_ubench_lds", "fa_ubench_mfma_bf16", "fa_ubench_mfma_valu",
+        "fa_device_info", "fa_ubench_copy", "fa_ubench_lds", "fa_ubench_mfma_bf16", "fa_ubench_mfma_mix", "fa_ubench_mfma_valu",
         "fa_ubench_valu"]
 
 
@@ -324,6 +324,10 @@ def test_ubench_argument_checks():
     assert fa.fa_ubench_mfma_valu(A, 1, 1, 4, 0, 2, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_mfma_valu(None, 1, 1, 4, 0, 0, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_mfma_valu(A, 0, 1, 4, 0, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_mix(A, 1, 1, 2, None) == fa.FA_ERR_INVALID_ARG  # mix not 0 or 1
+    assert fa.fa_ubench_mfma_mix(None, 1, 1, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_mix(A, 0, 1, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_mix(A, 1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_copy(A + 8, A + 4096, 256, 8, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_copy(A, A + 4096, 256, 0, None) == fa.FA_ERR_INVALID_ARG
 
