@@ -2,7 +2,7 @@
 //
 // One workgroup per (sequence, head, query tile), so one head is spread over many
 // compute units ("FlashAttention-2 (PT)", "2. Paralelismo aprimorado"). Four waves;
-// each wave owns QB blocks of 32 query rows whose Q fragments stay in registers for
+// each wave owns one block of 32 query rows whose Q fragments stay in registers for
 // the whole kernel. Key/value tiles of 64 rows are staged through LDS ("Tiling" in the
 // AI Atlas summary; "Aperçu technique" on aiunderstanding.org) and each wave computes
 //     S^T = K Q^T          (v_mfma_f32_32x32x16_bf16, fp32 accumulators)
@@ -13,10 +13,10 @@
 // work plus one lane swap, with no LDS round trip ("3. Divisão de trabalho otimizada
 // dentro do bloco"). Non-matmul work is kept small ("1. Minimização de operações não
 // matriciais"): the scale is folded into the exponent, c = scale * log2(e); the
-// division by l happens once at the end; and the output is rescaled only when some
-// row's running maximum has grown by more than 2^8 since the last rescale (until then
-// the stale maximum keeps every exponent <= 2^8, so nothing overflows and O and l keep
-// one common reference, which is all exactness needs).
+// division by l happens once at the end; and the output is rescaled only when a key
+// block's exponentials, formed under the current reference maximum, would grow too
+// large (a lane's share of a row sum above 2^8; until then nothing overflows and O and
+// l keep one common reference, which is all exactness needs).
 //
 // Data movement: K and V tiles are copied row-major into LDS by the global->LDS DMA
 // path (global_load_lds_dwordx4: no registers, no LDS write instructions); the copy of
@@ -43,14 +43,15 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-// Four waves per workgroup. With two 32-query blocks per wave (one wave per SIMD, 512
-// registers) every K and V operand read from LDS feeds two MFMAs; with one block, two
-// workgroups share a compute unit (256 registers per wave).
-template <int QB> constexpr int fwd_waves() { return 4; }
-template <int QB> constexpr int fwd_occupancy() { return QB == 1 ? 2 : 1; }
+// Four waves per workgroup, one 32-query block per wave. Workgroups per compute unit:
+// two at head_dim 128 (256 registers per wave), three at 64, whose Q and O fragments
+// fit 168. (Two query blocks per wave at one wave per SIMD, which halves the LDS reads
+// per MFMA, measured 6-23 % slower at head_dim 64: no other wave covers the waits
+// between the score MFMAs, the softmax and P.V.)
+constexpr int kFwdWaves = 4;
+template <int D> constexpr int fwd_occupancy() { return D == 64 ? 3 : 2; }
 constexpr int kFwdBC = 64;        // keys per tile
-constexpr float kRescaleTau = 8.f;  // log2 growth of the row max tolerated before rescaling
-constexpr float kKeepSum = 256.f;  // 2^tau: bound on a lane's share of a block's row sum (one block per wave)
+constexpr float kKeepSum = 256.f;  // 2^8: bound on a lane's share of a block's row sum
 
 template <int D>
 struct FwdLds {
@@ -61,13 +62,13 @@ struct FwdLds {
   static constexpr int BUF = KSZ + VSZ;
 };
 
-template <int D, int QB>
+template <int D>
 struct FwdState {
   static constexpr int NB = D / 32;
-  bf16x8 qf[QB][D / 16];
-  f32x16 oacc[QB][NB];
-  float m_run[QB];  // reference maximum of the raw scores q.k of this lane's query
-  float l_run[QB];  // this lane's share of sum_j exp2(c * (s_j - m_run))
+  bf16x8 qf[D / 16];
+  f32x16 oacc[NB];
+  float m_run;  // reference maximum of the raw scores q.k of this lane's query
+  float l_run;  // this lane's share of sum_j exp2(c * (s_j - m_run))
 };
 
 // The tile loop is software-pipelined by hand. A 64-key tile is two 32-key blocks, and
@@ -80,22 +81,6 @@ struct FwdState {
 // per read).
 
 constexpr int kFwdPf = 3;
-
-// O^T += V^T P^T step. With two query blocks per wave the O accumulators live in AGPRs
-// (see mfma32_agpr); with one they stay in VGPRs like everything else.
-template <int QB>
-__device__ __forceinline__ void fwd_pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  if constexpr (QB == 2) {
-    mfma32_agpr(acc, a, b);
-  } else {
-    acc = mfma32(a, b, acc);
-  }
-}
-
-template <int QB>
-__device__ __forceinline__ void fwd_o_fence(f32x16& acc) {
-  if constexpr (QB == 2) agpr_acc_fence(acc);
-}
 
 // K operand of S step s for key block j: row 32j + lane % 32 of the tile, head-dim
 // entries 16s + 8(lane / 32) + 0..7.
@@ -111,131 +96,15 @@ __device__ __forceinline__ bf16x8 fwd_v_operand(const u16* Vs, int bb, int t, in
   return lds_tr_operand(Vs, FwdLds<D>::VP, 16 * t, 32 * bb, lane);
 }
 
-// Block j's scores: mask, row maxima (into m_new) and whether O and l need a rescale:
-// some row's maximum grew by more than 2^tau (always so on the first visible block,
-// where m_run is -inf). The decision is taken for the whole wave.
-template <int D, int QB, bool CAUSAL>
-__device__ __forceinline__ bool fwd_block_stats(const FwdState<D, QB>& st, f32x16 (&sj)[QB], float (&m_new)[QB],
-                                                int kb0, int len, int wq0, int lane, float c, bool mask) {
-  const int lr = lane & 31, g = lane >> 5;
-  bool grow = false;
-#pragma unroll
-  for (int n = 0; n < QB; ++n) {
-    const int qi = wq0 + 32 * n + lr;
-    if (mask) {  // wave-uniform: a diagonal or tail tile
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + crow_nat(r, g);
-        const bool hide = key >= len || (CAUSAL && key > qi);
-        sj[n][r] = hide ? -INFINITY : sj[n][r];
-      }
-    }
-    float mx = sj[n][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sj[n][r]);
-    m_new[n] = fmaxf(st.m_run[n], pair_max(mx));
-    grow |= (m_new[n] - st.m_run[n]) * c > kRescaleTau;
-  }
-  return __builtin_amdgcn_ballot_w64(grow) != 0;
-}
-
-// Move the reference maximum to m_new and scale l to match; returns the factor that O
-// must be scaled by (the caller does it once every product formed under the old
-// reference has been added).
-template <int D, int QB>
-__device__ __forceinline__ void fwd_move_ref(FwdState<D, QB>& st, const float (&m_new)[QB], float c,
-                                             float (&alpha)[QB]) {
-#pragma unroll
-  for (int n = 0; n < QB; ++n) {
-    const float m_to = m_new[n] == -INFINITY ? 0.f : m_new[n];
-    alpha[n] = fast_exp2((st.m_run[n] - m_to) * c);
-    st.m_run[n] = m_new[n];
-    st.l_run[n] *= alpha[n];
-  }
-}
-
-template <int D, int QB>
-__device__ __forceinline__ void fwd_scale_o(FwdState<D, QB>& st, const float (&alpha)[QB]) {
-#pragma unroll
-  for (int n = 0; n < QB; ++n)
-#pragma unroll
-    for (int bb = 0; bb < D / 32; ++bb) {
-      fwd_o_fence<QB>(st.oacc[n][bb]);
-      st.oacc[n][bb] *= alpha[n];
-    }
-}
-
-// With two query blocks per wave (one wave per SIMD) each exponential's uses are pinned
-// to the step after it; with one block (two waves per SIMD) they are left to the
-// compiler, which sinks them into the code between phases, where the other wave on
-// the SIMD covers them (measured: pinning costs 1 % at d=128 and gains 4 % at d=64).
-template <int QB>
-constexpr bool fwd_pin_uses() { return QB == 2; }
-
-// The use of exponential v of block j (value v of QB * 16): its share of the row sum
-// (the four partial sums start from values 0..3, not from 0 + x, which does not fold
-// away) and, every eighth value, the bf16 conversion of eight of them into P, pinned to
-// the step it is called in.
-template <int QB>
-__device__ __forceinline__ void fwd_exp_use(const f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4],
-                                            int v) {
-  const int n = v / 16, r = v % 16;
-  if (r < 4)
-    ls[n][r] = sj[n][r];
-  else
-    ls[n][r & 3] += sj[n][r];
-  asm volatile("" : "+v"(ls[n][r & 3]));
-  if (r % 8 == 7) {
-    pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
-    asm volatile("" : "+v"(pj[n][r / 8]));
-  }
-}
-
-// Exponential v of block j's scores, in place, and its uses: those of v - 1 when they
-// are pinned (a step apart, so no use waits on the transcendental result, which needs a
-// wait state; the phase then ends with fwd_exp_use of its last value), else its own.
-template <int QB>
-__device__ __forceinline__ void fwd_exp_one(f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4],
-                                            const float (&nb)[QB], float c, int v) {
-  const int n = v / 16, r = v % 16;
-  float e = fast_exp2(fmaf(sj[n][r], c, nb[n]));
-  // Pin the exponential to this step: without it the compiler sinks the whole softmax
-  // towards its first use, out of the matrix-pipe phase it is meant to overlap.
-  asm volatile("" : "+v"(e));
-  sj[n][r] = e;
-  if constexpr (fwd_pin_uses<QB>()) {
-    if (v > 0) fwd_exp_use<QB>(sj, pj, ls, v - 1);
-  } else {
-    ls[n][r & 3] += e;
-    if (r % 8 == 7) pj[n][r / 8] = to_bf16x8(half_of(sj[n], r / 8));
-  }
-}
-
-template <int QB>
-__device__ __forceinline__ void fwd_exp_end(const f32x16 (&sj)[QB], bf16x8 (&pj)[QB][2], float (&ls)[QB][4]) {
-  if constexpr (fwd_pin_uses<QB>()) fwd_exp_use<QB>(sj, pj, ls, 16 * QB - 1);
-}
-
-template <int QB>
-__device__ __forceinline__ void fwd_exp_begin(const float (&m_run)[QB], float c, float (&nb)[QB],
-                                              float (&ls)[QB][4]) {
-#pragma unroll
-  for (int n = 0; n < QB; ++n) {
-    nb[n] = m_run[n] == -INFINITY ? 0.f : -m_run[n] * c;
-    if constexpr (!fwd_pin_uses<QB>()) ls[n][0] = ls[n][1] = ls[n][2] = ls[n][3] = 0.f;
-  }
-}
-
-// ---- One query block per wave (d = 128): the row-sum check instead of row maxima.
+// ---- The row-sum check instead of row maxima.
 // The exponentials of a 32-key block are formed under the current reference without
 // looking for the block's maximum first, and kept when every lane's share of each row sum
-// is at most 2^tau: then so is every single P, whatever the block's true maximum, which
-// is all the lazy rescale needs (O and l on one common reference, nothing overflows).
+// is at most 2^8: then so is every single P, whatever the block's true maximum, which is
+// all the lazy rescale needs (O and l on one common reference, nothing overflows).
 // Only before a query's first visible key, or when the check fails, does the reference
 // move to the block's exact maximum and the exponentials get formed again. The row sums
 // are formed anyway, so the common case trades a 16-value maximum, a lane swap and a
-// serial section per block for one compare. (With two blocks per wave the raw scores that
-// the uncommon path needs cost more than this saves.)
+// serial section per block for one compare.
 
 __device__ __forceinline__ float row_max16(const f32x16& x) {
   float mx = x[0];
@@ -246,7 +115,7 @@ __device__ __forceinline__ float row_max16(const f32x16& x) {
 
 // Hide the scores of block j (keys kb0 .. kb0 + 31) that the query does not see.
 template <bool CAUSAL>
-__device__ __forceinline__ void fwd1_mask(f32x16& sj, int kb0, int len, int wq0, int lane) {
+__device__ __forceinline__ void fwd_mask(f32x16& sj, int kb0, int len, int wq0, int lane) {
   const int qi = wq0 + (lane & 31), g = lane >> 5;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -257,7 +126,7 @@ __device__ __forceinline__ void fwd1_mask(f32x16& sj, int kb0, int len, int wq0,
 
 // Exponential r of the block (the raw scores stay), its share of the row sum and, every
 // eighth, the bf16 conversion of eight of them into P.
-__device__ __forceinline__ void fwd1_exp_one(const f32x16& sj, f32x8& ev, bf16x8 (&pj)[2], float (&ls)[4], float nb,
+__device__ __forceinline__ void fwd_exp_one(const f32x16& sj, f32x8& ev, bf16x8 (&pj)[2], float (&ls)[4], float nb,
                                              float c, int r) {
   float e = fast_exp2(fmaf(sj[r], c, nb));
   // Pin the exponential (and below the conversion) to this step: the compiler would sink
@@ -272,7 +141,7 @@ __device__ __forceinline__ void fwd1_exp_one(const f32x16& sj, f32x8& ev, bf16x8
 }
 
 // Whether the block's exponentials stand (see above); decided for the whole wave.
-__device__ __forceinline__ bool fwd1_keep(float m_run, const f32x16& sj, float bsum) {
+__device__ __forceinline__ bool fwd_keep(float m_run, const f32x16& sj, float bsum) {
   bool redo = !(bsum <= kKeepSum);
   if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0)  // before some query's first visible key
     redo |= m_run == -INFINITY && row_max16(sj) > -INFINITY;
@@ -283,15 +152,14 @@ __device__ __forceinline__ bool fwd1_keep(float m_run, const f32x16& sj, float b
 // (which holds only products formed under the old reference) are scaled to match, and
 // the block's exponentials are formed again.
 template <int D>
-__device__ __forceinline__ void fwd1_redo(FwdState<D, 1>& st, const f32x16& sj, bf16x8 (&pj)[2], float& bsum,
-                                          float c) {
-  const float m_new = fmaxf(st.m_run[0], pair_max(row_max16(sj)));
+__device__ __forceinline__ void fwd_redo(FwdState<D>& st, const f32x16& sj, bf16x8 (&pj)[2], float& bsum, float c) {
+  const float m_new = fmaxf(st.m_run, pair_max(row_max16(sj)));
   const float m_to = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2((st.m_run[0] - m_to) * c);
-  st.m_run[0] = m_new;
-  st.l_run[0] *= alpha;
+  const float alpha = fast_exp2((st.m_run - m_to) * c);
+  st.m_run = m_new;
+  st.l_run *= alpha;
 #pragma unroll
-  for (int bb = 0; bb < D / 32; ++bb) st.oacc[0][bb] *= alpha;
+  for (int bb = 0; bb < D / 32; ++bb) st.oacc[bb] *= alpha;
   const float nb = -m_to * c;
   f32x8 ev;
   float sum = 0.f;
@@ -304,9 +172,10 @@ __device__ __forceinline__ void fwd1_redo(FwdState<D, 1>& st, const f32x16& sj, 
   bsum = sum;
 }
 
+// One key tile for one wave: S^T = K Q^T, softmax update, O^T += V^T P^T.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, const u16* Vs, int k0, int len,
-                                            int wq0, int lane, float c, bool mask) {
+__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u16* Vs, int k0, int len, int wq0,
+                                         int lane, float c, bool mask) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int TP = 2 * NB;  // PV steps per key block
   static_assert(16 % NS == 0 && 16 % TP == 0, "exponentials must split evenly over the steps");
@@ -319,17 +188,17 @@ __device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, c
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 0, s + kFwdPf, lane);
-      s0 = mfma32(a[s], st.qf[0][s], s0);
+      s0 = mfma32(a[s], st.qf[s], s0);
       step_fence();
     }
   }
-  if (mask) fwd1_mask<CAUSAL>(s0, k0, len, wq0, lane);  // wave-uniform: a diagonal or tail tile
+  if (mask) fwd_mask<CAUSAL>(s0, k0, len, wq0, lane);  // wave-uniform: a diagonal or tail tile
 
   // S_1 with exp(S_0)
   bf16x8 p0[2], p1[2];
   f32x8 ev;
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
-  float nb = st.m_run[0] == -INFINITY ? 0.f : -st.m_run[0] * c;
+  float nb = st.m_run == -INFINITY ? 0.f : -st.m_run * c;
   {
     bf16x8 a[NS];
 #pragma unroll
@@ -337,21 +206,21 @@ __device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, c
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 1, s + kFwdPf, lane);
-      s1 = mfma32(a[s], st.qf[0][s], s1);
+      s1 = mfma32(a[s], st.qf[s], s1);
 #pragma unroll
-      for (int u = 0; u < 16 / NS; ++u) fwd1_exp_one(s0, ev, p0, ls, nb, c, s * (16 / NS) + u);
+      for (int u = 0; u < 16 / NS; ++u) fwd_exp_one(s0, ev, p0, ls, nb, c, s * (16 / NS) + u);
       step_fence();
     }
   }
   float bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  if (!fwd1_keep(st.m_run[0], s0, bsum)) fwd1_redo<D>(st, s0, p0, bsum, c);
-  st.l_run[0] += bsum;
-  if (mask) fwd1_mask<CAUSAL>(s1, k0 + 32, len, wq0, lane);
+  if (!fwd_keep(st.m_run, s0, bsum)) fwd_redo<D>(st, s0, p0, bsum, c);
+  st.l_run += bsum;
+  if (mask) fwd_mask<CAUSAL>(s1, k0 + 32, len, wq0, lane);
 
   // P_0 V_0 with exp(S_1). If block 1 then moves the reference, P_0 (formed under the
   // old one) has joined O already and is scaled with the rest of it.
   ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
-  nb = st.m_run[0] == -INFINITY ? 0.f : -st.m_run[0] * c;
+  nb = st.m_run == -INFINITY ? 0.f : -st.m_run * c;
   {
     bf16x8 a[TP];
 #pragma unroll
@@ -359,15 +228,15 @@ __device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, c
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
       if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, (i + kFwdPf) & 1, lane);
-      st.oacc[0][i >> 1] = mfma32(a[i], p0[i & 1], st.oacc[0][i >> 1]);
+      st.oacc[i >> 1] = mfma32(a[i], p0[i & 1], st.oacc[i >> 1]);
 #pragma unroll
-      for (int u = 0; u < 16 / TP; ++u) fwd1_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
+      for (int u = 0; u < 16 / TP; ++u) fwd_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
       step_fence();
     }
   }
   bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  if (!fwd1_keep(st.m_run[0], s1, bsum)) fwd1_redo<D>(st, s1, p1, bsum, c);
-  st.l_run[0] += bsum;
+  if (!fwd_keep(st.m_run, s1, bsum)) fwd_redo<D>(st, s1, p1, bsum, c);
+  st.l_run += bsum;
 
   // P_1 V_1
   {
@@ -377,103 +246,7 @@ __device__ __forceinline__ void fwd_tile_q1(FwdState<D, 1>& st, const u16* Ks, c
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
       if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, 2 + ((i + kFwdPf) & 1), lane);
-      st.oacc[0][i >> 1] = mfma32(a[i], p1[i & 1], st.oacc[0][i >> 1]);
-      step_fence();
-    }
-  }
-}
-
-// One key tile for one wave: S^T = K Q^T, softmax update, O^T += V^T P^T.
-template <int D, int QB, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, const u16* Vs, int k0, int len,
-                                         int wq0, int lane, float c, bool mask) {
-  if constexpr (QB == 1) {
-    fwd_tile_q1<D, CAUSAL>(st, Ks, Vs, k0, len, wq0, lane, c, mask);
-    return;
-  }
-  constexpr int NS = D / 16, NB = D / 32, E = 16 * QB;
-  constexpr int TP = 2 * NB;  // PV steps per key block: (bb, t) for t in the block's two slices
-  static_assert(E % NS == 0 && E % TP == 0, "exponentials must split evenly over the steps");
-
-  f32x16 s0[QB], s1[QB];
-#pragma unroll
-  for (int n = 0; n < QB; ++n) s0[n] = s1[n] = f32x16{};
-
-  // S_0
-  {
-    bf16x8 a[NS];
-#pragma unroll
-    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 0, s, lane);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 0, s + kFwdPf, lane);
-#pragma unroll
-      for (int n = 0; n < QB; ++n) s0[n] = mfma32(a[s], st.qf[n][s], s0[n]);
-      step_fence();
-    }
-  }
-  float m_new[QB], alpha[QB];
-  if (fwd_block_stats<D, QB, CAUSAL>(st, s0, m_new, k0, len, wq0, lane, c, mask)) {
-    fwd_move_ref<D, QB>(st, m_new, c, alpha);
-    fwd_scale_o<D, QB>(st, alpha);
-  }
-
-  // S_1 with exp(S_0)
-  bf16x8 p0[QB][2], p1[QB][2];
-  float nb[QB], ls[QB][4];
-  fwd_exp_begin<QB>(st.m_run, c, nb, ls);
-  {
-    bf16x8 a[NS];
-#pragma unroll
-    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 1, s, lane);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 1, s + kFwdPf, lane);
-#pragma unroll
-      for (int n = 0; n < QB; ++n) s1[n] = mfma32(a[s], st.qf[n][s], s1[n]);
-#pragma unroll
-      for (int u = 0; u < E / NS; ++u) fwd_exp_one<QB>(s0, p0, ls, nb, c, s * (E / NS) + u);
-      step_fence();
-    }
-    fwd_exp_end<QB>(s0, p0, ls);
-  }
-#pragma unroll
-  for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
-  const bool grow1 = fwd_block_stats<D, QB, CAUSAL>(st, s1, m_new, k0 + 32, len, wq0, lane, c, mask);
-  if (grow1) fwd_move_ref<D, QB>(st, m_new, c, alpha);
-
-  // P_0 V_0 with exp(S_1). If block 1 moved the reference maximum, P_0 (formed under
-  // the old one) still joins O first and O is scaled right after.
-  fwd_exp_begin<QB>(st.m_run, c, nb, ls);
-  {
-    bf16x8 a[TP];
-#pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, i & 1, lane);
-#pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, (i + kFwdPf) & 1, lane);
-#pragma unroll
-      for (int n = 0; n < QB; ++n) fwd_pv_mfma<QB>(st.oacc[n][i >> 1], a[i], p0[n][i & 1]);
-#pragma unroll
-      for (int u = 0; u < E / TP; ++u) fwd_exp_one<QB>(s1, p1, ls, nb, c, i * (E / TP) + u);
-      step_fence();
-    }
-    fwd_exp_end<QB>(s1, p1, ls);
-  }
-#pragma unroll
-  for (int n = 0; n < QB; ++n) st.l_run[n] += (ls[n][0] + ls[n][1]) + (ls[n][2] + ls[n][3]);
-  if (grow1) fwd_scale_o<D, QB>(st, alpha);
-
-  // P_1 V_1
-  {
-    bf16x8 a[TP];
-#pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, 2 + (i & 1), lane);
-#pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, 2 + ((i + kFwdPf) & 1), lane);
-#pragma unroll
-      for (int n = 0; n < QB; ++n) fwd_pv_mfma<QB>(st.oacc[n][i >> 1], a[i], p1[n][i & 1]);
+      st.oacc[i >> 1] = mfma32(a[i], p1[i & 1], st.oacc[i >> 1]);
       step_fence();
     }
   }
@@ -481,12 +254,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, QB>& st, const u16* Ks, con
 
 // One query tile of one (sequence, head): the key loop and the epilogue. The two LDS
 // buffers are free again when it returns (its last step ends in a barrier).
-template <int D, bool CAUSAL, bool VARLEN, int QB, bool DESC = false>
+template <int D, bool CAUSAL, bool VARLEN, bool DESC = false>
 __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int start, int len, int qt, u16* buf0,
                                           u16* buf1) {
 #if __HIP_DEVICE_COMPILE__
-  constexpr int NW = fwd_waves<QB>();
-  constexpr int BR = 32 * QB * NW, BC = kFwdBC;
+  constexpr int NW = kFwdWaves;
+  constexpr int BR = 32 * NW, BC = kFwdBC;
   constexpr int NB = D / 32, NS = D / 16;
   using L = FwdLds<D>;
   const int tid = threadIdx.x;
@@ -500,22 +273,14 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
   const u16* __restrict__ Kg = p.k + base;
   const u16* __restrict__ Vg = p.v + base;
 
-  const int wq0 = q0 + 32 * QB * w;  // first query row of this wave
-  const int wq_last = min(wq0 + 32 * QB - 1, len - 1);
+  const int wq0 = q0 + 32 * w;  // first query row of this wave
+  const int wq_last = min(wq0 + 31, len - 1);
 
-  FwdState<D, QB> st;
+  FwdState<D> st;
 #pragma unroll
-  for (int n = 0; n < QB; ++n) {
-    const int qi = wq0 + 32 * n + lr;
-    if constexpr (QB != 1)  // one block per wave: Q comes in through LDS below
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        st.qf[n][s] = qi < len ? ld16(Qg + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) st.oacc[n][bb] = f32x16{};
-    st.m_run[n] = -INFINITY;
-    st.l_run[n] = 0.f;
-  }
+  for (int bb = 0; bb < NB; ++bb) st.oacc[bb] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
@@ -537,16 +302,15 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
     // wave-uniform: skip tiles that are entirely masked for this wave
     if (wq0 < len && (!CAUSAL || k0 <= wq_last)) {
       const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);
-      fwd_tile<D, QB, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
+      fwd_tile<D, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
     }
   };
-  // Two LDS buffers in turn: the copy of tile kt+1 is in flight while tile kt is used.
-  if constexpr (QB == 1) {
-    // The tile's Q rows come in through buf1 (whole-row copies; loaded straight into
-    // registers, every load instruction would gather 32 bytes from each of 32 rows) while
-    // K/V tile 0 lands in buf0; every wave takes its rows before tile 1 refills buf1.
-    // The first barrier lets every wave finish reading the previous query tile's O rows
-    // out of buf1.
+  // The tile's Q rows come in through buf1 (whole-row copies; loaded straight into
+  // registers, every load instruction would gather 32 bytes from each of 32 rows) while
+  // K/V tile 0 lands in buf0; every wave takes its rows before tile 1 refills buf1.
+  // The first barrier lets every wave finish reading the previous query tile's O rows
+  // out of buf1.
+  {
     constexpr int QP = D + 8;  // row pitch of the staged Q rows: conflict-free row reads
     static_assert(BR * QP <= L::BUF, "the Q tile fits in one buffer");
     __syncthreads();
@@ -559,17 +323,10 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
     const int qi = wq0 + lr;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      st.qf[0][s] = qi < len ? ld16(buf1 + (32 * w + lr) * QP + 16 * s + 8 * g) : zero_bf16x8();
-    __syncthreads();
-  } else {
-    issue(0, buf0);
-#pragma unroll
-    for (int n = 0; n < QB; ++n)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) settle(st.qf[n][s]);
-    wait_vmem();
+      st.qf[s] = qi < len ? ld16(buf1 + (32 * w + lr) * QP + 16 * s + 8 * g) : zero_bf16x8();
     __syncthreads();
   }
+  // Two LDS buffers in turn: the copy of tile kt+1 is in flight while tile kt is used.
   for (int kt = 0; kt < n_kt; kt += 2) {
     if (kt + 1 < n_kt) issue(kt + 1, buf1);
     compute(kt, buf0);
@@ -582,44 +339,23 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
     __syncthreads();
   }
 
-#pragma unroll
-  for (int n = 0; n < QB; ++n)
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) fwd_o_fence<QB>(st.oacc[n][bb]);
-  // With one query block per wave, the tiles being consumed (the loop ends on a barrier),
-  // buf1 stages O so that its rows leave whole (buf1, since a workgroup's next query tile
-  // starts by copying into buf0; its first barrier comes after these reads). With two,
-  // the O accumulators sit in AGPRs and staging cost the tile loop registers (measured
-  // slower at long sequences), so those rows are stored directly.
+  // The tiles being consumed (the loop ends on a barrier), buf1 stages O so that its rows
+  // leave whole (buf1, since a workgroup's next query tile starts by copying into buf0;
+  // its first barrier comes after these reads).
   static_assert(NW * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
   u16* stg = buf1 + w * 32 * stage_pitch<D>();
-#pragma unroll
-  for (int n = 0; n < QB; ++n) {
-    const int qi = wq0 + 32 * n + lr;
-    const float l_tot = pair_sum(st.l_run[n]);
-    if constexpr (QB == 1) {
-      stage_acc_rows<D>(stg, st.oacc[n], 1.f / l_tot, lr, g);
-      store_staged_rows<D, 32>(stg, p.o + base + (size_t)wq0 * stride, stride, len - wq0, lane);
-    } else if (qi < len) {
-      const float inv = 1.f / l_tot;
-      u16* __restrict__ Og = p.o + base + (size_t)qi * stride;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)  // lane group g: head-dim entries 32bb + 8a + 4g + {0..3}
-          store_bf16x4(Og + 32 * bb + 8 * a + 4 * g, st.oacc[n][bb][4 * a] * inv, st.oacc[n][bb][4 * a + 1] * inv,
-                       st.oacc[n][bb][4 * a + 2] * inv, st.oacc[n][bb][4 * a + 3] * inv);
-    }
-    if (g == 0 && qi < len) {
-      const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
-      p.lse[li] = st.m_run[n] * p.scale + logf(l_tot);
-    }
+  const int qi = wq0 + lr;
+  const float l_tot = pair_sum(st.l_run);
+  stage_acc_rows<D>(stg, st.oacc, 1.f / l_tot, lr, g);
+  store_staged_rows<D, 32>(stg, p.o + base + (size_t)wq0 * stride, stride, len - wq0, lane);
+  if (g == 0 && qi < len) {
+    const size_t li = VARLEN ? (size_t)h * p.T + start + qi : ((size_t)b * p.H + h) * p.N + qi;
+    p.lse[li] = st.m_run * p.scale + logf(l_tot);
   }
 #endif
 }
 
-// Two query blocks per wave need the whole register file (one workgroup per compute
-// unit). Workgroup -> (sequence, head, slot): head-grouped per XCD, so the workgroups
+// Workgroup -> (sequence, head, slot): head-grouped per XCD, so the workgroups
 // resident on one XCD share few heads and stream the same K/V rows through its L2 (this
 // keeps the fabric traffic near the O(N d) operand bytes at long sequences). Without
 // masking a slot is one query tile; under causal masking tile t visits t + 1 key tiles,
@@ -629,9 +365,9 @@ __device__ __forceinline__ void fwd_qtile(const FwdParams& p, int b, int h, int 
 // same step for every workgroup, so at any moment the co-resident workgroups of a head
 // read two key tiles between them (one in each direction) and the head's K/V passes
 // through L2 about once, however long the sequence.
-template <int D, bool CAUSAL, bool VARLEN, int QB>
-__global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int BR = 32 * QB * fwd_waves<QB>();
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(64 * kFwdWaves, fwd_occupancy<D>()) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int BR = 32 * kFwdWaves;
   using L = FwdLds<D>;
   __shared__ __attribute__((aligned(16))) u16 buf0[L::BUF];
   __shared__ __attribute__((aligned(16))) u16 buf1[L::BUF];
@@ -651,11 +387,11 @@ __global__ __launch_bounds__(64 * fwd_waves<QB>(), fwd_occupancy<QB>()) void fwd
   if (CAUSAL) {
     const int t_hi = nt - 1 - slot;
     if (t_hi < slot) return;
-    fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, t_hi, buf0, buf1);
-    if (slot < t_hi) fwd_qtile<D, CAUSAL, VARLEN, QB, true>(p, b, h, start, len, slot, buf0, buf1);
+    fwd_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, t_hi, buf0, buf1);
+    if (slot < t_hi) fwd_qtile<D, CAUSAL, VARLEN, true>(p, b, h, start, len, slot, buf0, buf1);
   } else {
     if (slot >= nt) return;
-    fwd_qtile<D, CAUSAL, VARLEN, QB>(p, b, h, start, len, slot, buf0, buf1);
+    fwd_qtile<D, CAUSAL, VARLEN>(p, b, h, start, len, slot, buf0, buf1);
   }
 }
 
@@ -700,14 +436,14 @@ __global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
   const u16* __restrict__ Vg = p.v + ((size_t)b * p.Nk * p.H + h) * D + (size_t)ks * stride;
   const int len = ke - ks;  // keys of this split, rows 0..len-1 of Kg / Vg
 
-  FwdState<D, 1> st;
+  FwdState<D> st;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    st.qf[0][s] = lr < p.Nq ? ld16(Qg + (size_t)lr * stride + 16 * s + 8 * g) : zero_bf16x8();
+    st.qf[s] = lr < p.Nq ? ld16(Qg + (size_t)lr * stride + 16 * s + 8 * g) : zero_bf16x8();
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) st.oacc[0][bb] = f32x16{};
-  st.m_run[0] = -INFINITY;
-  st.l_run[0] = 0.f;
+  for (int bb = 0; bb < NB; ++bb) st.oacc[bb] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 
   TileDma<BC, D, L::KP, 1> kdma;
   TileDma<BC, D, L::VP, 1> vdma;
@@ -724,12 +460,12 @@ __global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
   auto step = [&](int kt, const u16* buf) {
     const int k0 = kt * BC;
     const bool mask = k0 + BC > len || (CAUSAL && k0 + BC - 1 > wq0);  // wave-uniform
-    fwd_tile<D, 1, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
+    fwd_tile<D, CAUSAL>(st, buf, buf + L::KSZ, k0, len, wq0, lane, p.c, mask);
   };
   kdma.issue(buf0, Kg, 0, len, stride, w, lane);
   vdma.issue(buf0 + L::KSZ, Vg, 0, len, stride, w, lane);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) settle(st.qf[0][s]);
+  for (int s = 0; s < NS; ++s) settle(st.qf[s]);
   wait_vmem();
   for (int kt = 0; kt < n_kt; kt += 2) {
     // One wave: its LDS reads of a buffer are consumed by its MFMAs before the next
@@ -749,7 +485,7 @@ __global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
     wait_vmem();
   }
 
-  const float l_tot = pair_sum(st.l_run[0]);
+  const float l_tot = pair_sum(st.l_run);
   if (lr >= p.Nq) return;
   // A split can hold no key a query sees (causal): its weight in the merge is then 0.
   const bool empty = !(l_tot > 0.f);
@@ -761,13 +497,13 @@ __global__ __launch_bounds__(64, 1) void decode_split_kernel(DecParams p) {
     for (int a = 0; a < 4; ++a) {
       // lane group g holds head-dim entries 32bb + 8a + 4g + {0..3} in registers 4a..4a+3
       *reinterpret_cast<f32x4*>(Po + 32 * bb + 8 * a + 4 * g) =
-          f32x4{st.oacc[0][bb][4 * a] * inv, st.oacc[0][bb][4 * a + 1] * inv, st.oacc[0][bb][4 * a + 2] * inv,
-                st.oacc[0][bb][4 * a + 3] * inv};
+          f32x4{st.oacc[bb][4 * a] * inv, st.oacc[bb][4 * a + 1] * inv, st.oacc[bb][4 * a + 2] * inv,
+                st.oacc[bb][4 * a + 3] * inv};
     }
   }
   if (g == 0)
     p.part_lse[((size_t)bh * p.n_splits + split) * p.Nq + lr] =
-        empty ? -INFINITY : st.m_run[0] * p.scale + logf(l_tot);
+        empty ? -INFINITY : st.m_run * p.scale + logf(l_tot);
 }
 
 // One wave per (sequence, head, query): lse = log sum_s exp(lse_s), O = sum_s
@@ -832,10 +568,7 @@ hipError_t launch_decode_t(const DecodeProblem& pr) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_fwd_t(const Problem& pr) {
-  // Two query blocks per wave halve the LDS reads per MFMA; at head_dim 128 their
-  // accumulators no longer fit the register file, so one block is used there.
-  constexpr int QB = D == 64 ? 2 : 1;
-  constexpr int BR = 32 * QB * fwd_waves<QB>();
+  constexpr int BR = 32 * kFwdWaves;
   FwdParams p;
   p.q = static_cast<const u16*>(pr.q);
   p.k = static_cast<const u16*>(pr.k);
@@ -852,7 +585,7 @@ hipError_t launch_fwd_t(const Problem& pr) {
   p.scale = pr.scale;
   p.c = pr.scale * kLog2e;
   const dim3 grid((unsigned)(p.n_slots * pr.batch * pr.heads));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, QB>), grid, dim3(64 * fwd_waves<QB>()), 0, pr.stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(64 * kFwdWaves), 0, pr.stream, p);
   return hipGetLastError();
 }
 
