@@ -6,9 +6,10 @@
 // Three kernels:
 //   bwd_pre   D_i = sum_k dO_ik * O_ik for every query row (fp32), from the stored O,
 //             and -LSE_i / scale, the starting value of the S accumulation in bwd_dkdv.
-//   bwd_dkdv  one workgroup per (sequence, head, 128-key tile); each wave owns 32 keys
-//             and keeps K, V fragments and the dK^T, dV^T accumulators in registers
-//             while it walks the 64-query tiles:
+//   bwd_dkdv  one (sequence, head, 128-key tile) at a time per workgroup (at head_dim
+//             128 one persistent workgroup per compute unit takes a list of them); each
+//             wave owns 32 keys and keeps K, V fragments and the dK^T, dV^T
+//             accumulators in registers while it walks the 64-query tiles:
 //                 S  = Q K^T,  P = exp2(c S - LSE log2e)
 //                 dP = dO V^T, dS = P * (dP - D)
 //                 dV^T += dO^T P,  dK^T += Q^T dS
@@ -386,7 +387,7 @@ __device__ __forceinline__ void kv_x(bool nxt, bool cur, bool mask, const KvStat
 #undef FA_KV_X
 }
 
-// One workgroup per (sequence, head, 128-key tile); wave w owns keys k0 + 32w .. + 31
+// One (sequence, head, 128-key tile) for one workgroup; wave w owns keys k0 + 32w .. + 31
 // and walks the 64-query tiles from the diagonal on, two 32-query blocks per tile, in a
 // software pipeline across blocks and tiles:
 //   X(t,0) [S, dP of (t,1) | softmax of (t,0)]  barrier  Y(t,0) [dV, dK of (t,0)]
@@ -395,22 +396,15 @@ __device__ __forceinline__ void kv_x(bool nxt, bool cur, bool mask, const KvStat
 // t+3 into the buffer tile t-1 used; a wave's last read of tile t-1 (in Y(t-1,1))
 // comes before it.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
-  static_assert(D == 128, "head_dim 64 has its own kernel (bwd_dkdv_rows_kernel)");
+__device__ __forceinline__ void dkdv_ktile(const BwdParams& p, int bh, int kt, u16* lds) {
   constexpr int BK = kKvBK, BQ = kKvBQ, NS = D / 16, NB = D / 32;
   constexpr int S = kKvStages;
   using L = KvLds<D>;
   using Dma = TileDma<BQ, D, L::P, kKvWaves, true, 8, false>;  // statistics in the pads of Q rows 0..7
-  __shared__ __attribute__((aligned(16))) u16 lds[S * L::BUF];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-
-  // Workgroup -> (sequence, head, key tile), head-grouped per XCD (the head's Q and dO
-  // stay in L2); under causal the first key tiles see the most queries and come first.
-  int bh, kt;
-  xcd_tile_map(blockIdx.x, p.B * p.H, p.n_tiles, false, true, bh, kt);
   const int b = bh / p.H, h = bh % p.H;
   int start, len;
   if (VARLEN) {
@@ -588,6 +582,28 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams 
   const int valid = len - wk0;
   store_staged_rows<D, 32>(stg, p.dk + base + (size_t)wk0 * stride, stride, valid, lane);
   store_staged_rows<D, 32>(stg + 32 * stage_pitch<D>(), p.dv + base + (size_t)wk0 * stride, stride, valid, lane);
+}
+
+// Persistent: gridDim.x = 8 C workgroups, one per compute unit; workgroup c of XCD x
+// (workgroup index 8 c + x) takes the XCD's work items k = n C + c in even rounds n and
+// n C + C - 1 - c in odd ones (item k of XCD x is the mapped tile 8 k + x), so that under
+// causal masking a heavy key tile and a light one alternate on each compute unit. A
+// workgroup's final stores then drain while it starts its next tile.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "head_dim 64 has its own kernel (bwd_dkdv_rows_kernel)");
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvStages * KvLds<D>::BUF];
+  const int total = p.B * p.H * p.n_tiles;
+  const int xcd = blockIdx.x % 8, c = blockIdx.x / 8, C = gridDim.x / 8;
+  for (int n = 0;; ++n) {
+    const int k = n * C + ((n & 1) ? C - 1 - c : c);
+    const int item = 8 * k + xcd;
+    if (item >= total) break;
+    int bh, kt;
+    xcd_tile_map(item, p.B * p.H, p.n_tiles, false, true, bh, kt);
+    if (n > 0) __syncthreads();  // every wave has read its staged rows of the previous tile
+    dkdv_ktile<D, CAUSAL, VARLEN>(p, bh, kt, lds);
+  }
 }
 
 // ------------------------------------------------------------------------ bwd_fused
@@ -1551,6 +1567,19 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(BwdParams p)
 
 // ------------------------------------------------------------------------ launch
 
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 BwdParams make_params(const Problem& pr) {
   BwdParams p;
   p.q = static_cast<const u16*>(pr.q);
@@ -1596,10 +1625,13 @@ hipError_t launch_dkdv_t(const Problem& pr) {
   BwdParams p = make_params(pr);
   p.n_tiles = (pr.seqlen + kKvBK - 1) / kKvBK;
   const dim3 grid((unsigned)(p.n_tiles * pr.batch * pr.heads));
-  if constexpr (D == 64)
+  if constexpr (D == 64) {
     hipLaunchKernelGGL((bwd_dkdv_rows_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>), grid, dim3(kKvThreads), 0, pr.stream, p);
+  } else {
+    const int ncu = device_cu_count();
+    const unsigned g = (unsigned)(ncu >= 8 ? ncu / 8 * 8 : 8);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, VARLEN>), dim3(g), dim3(kKvThreads), 0, pr.stream, p);
+  }
   return hipGetLastError();
 }
 
