@@ -1449,34 +1449,6 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
   const int wq_last = min(wq0 + 31, len - 1);
 
   DqState<D> st;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const size_t off = base + (size_t)qi * stride + 16 * s + 8 * g;
-    st.qf[s] = qi < len ? ld16(p.q + off) : zero_bf16x8();
-    st.dof[s] = qi < len ? ld16(p.dout + off) : zero_bf16x8();
-  }
-  const float lse = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] : INFINITY;
-  st.lse2 = lse * kLog2e;
-  if constexpr (STATS) {
-    // lanes l and l ^ 32 hold the two halves of the row (head-dim 16 s + 8 g + 0..7)
-    float part = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 o8 = qi < len ? ld16(p.o + base + (size_t)qi * stride + 16 * s + 8 * g) : zero_bf16x8();
-      part = dot8_bf16(st.dof[s], o8, part);
-    }
-    st.dd = pair_sum(part);
-    if (g == 0 && qi < len) {
-      const size_t si = stat_index<VARLEN>(p, b, h, start, qi);
-      p.dvec_out[si] = st.dd;
-      p.mneg_out[si] = -lse / p.scale;
-    }
-  } else {
-    st.dd = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
-  }
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) st.dqT[bb] = f32x16{};
-
   const int kv_end = CAUSAL ? min(q0 + BR, len) : len;
   const int n_kt = (kv_end + BC - 1) / BC;
 
@@ -1498,16 +1470,52 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
       dq_tile<D, CAUSAL>(st, buf, k0, len, qi, lane, p.c, mask);
     }
   };
-  issue(0, buf0);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    settle(st.qf[s]);
-    settle(st.dof[s]);
-  }
-  settle(st.lse2);
-  settle(st.dd);
+
+  // The tile's Q and dO rows (and for the statistics O's) come in through the LDS
+  // buffers as whole-row copies: loaded straight into registers, every load instruction
+  // would gather 32 bytes from each of 32 rows. The first barrier lets every wave finish
+  // reading the previous query tile's staged dQ rows out of buf1.
+  constexpr int QP = D + 8;  // row pitch of the staged rows: conflict-free row reads
+  static_assert(BR * QP <= L::BUF, "a query tile's rows fit in one buffer");
+  const int er = (32 * w + lr) * QP + 8 * g;  // this lane's row, head-dim 8 g
+  TileDma<BR, D, QP, kDqWaves> rdma;
+  rdma.init(stride, w, lane);
+  __syncthreads();
+  rdma.issue(buf1, p.q + base, q0, len, stride, w, lane);
+  rdma.issue(buf0, p.dout + base, q0, len, stride, w, lane);
+  const float lse = qi < len ? p.lse[stat_index<VARLEN>(p, b, h, start, qi)] : INFINITY;
+  if constexpr (!STATS) st.dd = qi < len ? p.dvec[stat_index<VARLEN>(p, b, h, start, qi)] : 0.f;
   wait_vmem();
   __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    st.qf[s] = qi < len ? ld16(buf1 + er + 16 * s) : zero_bf16x8();
+    st.dof[s] = qi < len ? ld16(buf0 + er + 16 * s) : zero_bf16x8();
+  }
+  st.lse2 = lse * kLog2e;
+  __syncthreads();  // both buffers read
+  issue(0, buf0);
+  if constexpr (STATS) rdma.issue(buf1, p.o + base, q0, len, stride, w, lane);
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) st.dqT[bb] = f32x16{};
+  wait_vmem();
+  __syncthreads();
+  if constexpr (STATS) {
+    // lanes l and l ^ 32 hold the two halves of the row (head-dim 16 s + 8 g + 0..7)
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 o8 = qi < len ? ld16(buf1 + er + 16 * s) : zero_bf16x8();
+      part = dot8_bf16(st.dof[s], o8, part);
+    }
+    st.dd = pair_sum(part);
+    if (g == 0 && qi < len) {
+      const size_t si = stat_index<VARLEN>(p, b, h, start, qi);
+      p.dvec_out[si] = st.dd;
+      p.mneg_out[si] = -lse / p.scale;
+    }
+    __syncthreads();  // O read out of buf1 before tile 1 is copied there
+  }
   for (int kt = 0; kt < n_kt; kt += 2) {
     if (kt + 1 < n_kt) issue(kt + 1, buf1);
     compute(kt, buf0);
@@ -1521,8 +1529,8 @@ __device__ __forceinline__ void dq_qtile(const BwdParams& p, int b, int h, int s
   }
 
   // The tiles are consumed (the loop ends on a barrier): buf1 stages this wave's dQ rows
-  // so that they leave as whole rows (buf1, since a workgroup's next query tile starts
-  // by copying into buf0; its first barrier comes after these reads).
+  // so that they leave as whole rows (a workgroup's next query tile copies into the
+  // buffers only after its first barrier).
   static_assert(4 * 32 * stage_pitch<D>() <= L::BUF, "staging fits in one tile buffer");
   u16* stg = buf1 + w * 32 * stage_pitch<D>();
   stage_acc_rows<D>(stg, st.dqT, p.scale, lr, g);
