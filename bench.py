@@ -336,6 +336,8 @@ def ceilings(reps: int = 5):
     vblocks, viters = 32 * cus, 1000
     out = torch.empty(max(mblocks, vblocks) * 256, device="cuda", dtype=torch.float32)
     t_mfma = timed(lambda: ok(fa.fa_ubench_mfma_bf16(out.data_ptr(), mblocks, miters, sp), "mfma"))
+    m8iters = miters // 2                   # the 8-bit MFMA does four times the FLOPs in twice the time
+    t_mfma8 = timed(lambda: ok(fa.fa_ubench_mfma_fp8(out.data_ptr(), mblocks, m8iters, sp), "mfma fp8"))
     t_exp = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 0, sp), "exp"))
     t_fma = timed(lambda: ok(fa.fa_ubench_valu(out.data_ptr(), vblocks, viters, 1, sp), "fma"))
     lblocks, liters = 2 * cus, 4000          # two 64 KiB workgroups per CU (two waves per SIMD)
@@ -377,6 +379,7 @@ def ceilings(reps: int = 5):
         "device": info,
         "peak_bf16_tflops_from_clock": round(cus * BF16_FLOP_PER_CLK_CU * clk_hz / 1e12, 1),
         "mfma_bf16_loop_tflops": round(mfma_flops / (t_mfma * 1e-3) / 1e12, 1),
+        "mfma_fp8_loop_tflops": round(mblocks * 4 * m8iters * 8 * 131072.0 / (t_mfma8 * 1e-3) / 1e12, 1),
         "exp_gops": round(lane_ops / (t_exp * 1e-3) / 1e9, 1),
         "exp_lane_ops_per_clk_cu": round(lane_ops / (t_exp * 1e-3) / clk_hz / cus, 2),
         "fma_fp32_tflops": round(2 * lane_ops / (t_fma * 1e-3) / 1e12, 1),
@@ -391,7 +394,7 @@ def ceilings(reps: int = 5):
         "lds_tr_tbs": round(lblocks * 4 * liters * 8 * 1024 / (t_ldst * 1e-3) / 1e12, 1),
         "mfma_chain_cycles_per_mfma": coexec,
         "mfma_with_forward_mix": mix,
-        "ms": {"mfma": round(t_mfma, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
+        "ms": {"mfma": round(t_mfma, 4), "mfma_fp8": round(t_mfma8, 4), "exp": round(t_exp, 4), "fma": round(t_fma, 4), "copy": round(t_copy, 4),
                "lds_rows": round(t_ldsr, 4), "lds_tr": round(t_ldst, 4)},
         "note": "rates per clock use the reported maximum clock; the clock under load may be lower",
     }
@@ -701,6 +704,11 @@ def main(argv=None) -> int:
     if not a.no_fp8:
         log("bench: 8-bit forward")
         out["fp8_forward"] = fp8_bench(batch=a.batch, seqlen=a.seqlen)
+        if "ceilings" in out:
+            loop8 = out["ceilings"]["mfma_fp8_loop_tflops"]
+            for leg in out["fp8_forward"].values():
+                leg["peak_measured_mfma_loop"] = loop8
+                leg["frac_of_measured"] = round(leg["tflops"] / loop8, 4)
     if a.cpu_budget > 0:
         log(f"bench: CPU oracle baseline (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_budget)

@@ -26,7 +26,7 @@ __all__ = [
     "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
     "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes",
     "fa_strerror", "forward", "backward", "decode", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes",
-    "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_valu", "fa_ubench_lds", "fa_ubench_copy",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_info", "fa_ubench_mfma_bf16", "fa_ubench_mfma_fp8", "fa_ubench_valu", "fa_ubench_lds", "fa_ubench_copy",
     "fa_ubench_mfma_valu", "fa_ubench_mfma_mix",
 ]
 
@@ -95,6 +95,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_device_info.restype = i32
     lib.fa_ubench_mfma_bf16.argtypes = [vp, i32, i32, vp]
     lib.fa_ubench_mfma_bf16.restype = i32
+    lib.fa_ubench_mfma_fp8.argtypes = [vp, i32, i32, vp]
+    lib.fa_ubench_mfma_fp8.restype = i32
     lib.fa_ubench_valu.argtypes = [vp, i32, i32, i32, vp]
     lib.fa_ubench_valu.restype = i32
     lib.fa_ubench_lds.argtypes = [vp, i32, i32, i32, vp]
@@ -225,6 +227,10 @@ def fa_device_info(device: int = 0) -> dict:
 
 def fa_ubench_mfma_bf16(out: int, blocks: int, iters: int, stream: Optional[int]) -> int:
     return load_library().fa_ubench_mfma_bf16(out, blocks, iters, stream)
+
+
+def fa_ubench_mfma_fp8(out: int, blocks: int, iters: int, stream: Optional[int]) -> int:
+    return load_library().fa_ubench_mfma_fp8(out, blocks, iters, stream)
 
 
 def fa_ubench_valu(out: int, blocks: int, iters: int, op: int, stream: Optional[int]) -> int:

@@ -38,6 +38,32 @@ __global__ __launch_bounds__(kUbThreads) void ub_mfma_kernel(float* __restrict__
   out[(size_t)blockIdx.x * kUbThreads + tid] = s;
 }
 
+// The same for the 8-bit MFMA of the FP8 forward (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3
+// operands, block scales 2^0, 131072 FLOP each). Every operand byte is 0x30 .. 0x3f
+// (E4M3 0.5 .. 0.94), so no NaN code occurs.
+__global__ __launch_bounds__(kUbThreads) void ub_mfma_fp8_kernel(float* __restrict__ out, int iters) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const int tid = threadIdx.x;
+  const int x = (int)(0x38383838u ^ (uint32_t)(tid & 15) * 0x01010101u);
+  const int y = (int)(0x3a3a3a3au ^ (uint32_t)(blockIdx.x & 15) * 0x01010101u);
+  const i32x8 a = {x, y, x, y, x, y, x, y};
+  const i32x8 b = {y, x, y, x, y, x, y, x};
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, 0, 0, 0, 127, 0, 127);
+      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, 0, 0, 0, 127, 0, 127);
+      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, 0, 0, 0, 127, 0, 127);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[(size_t)blockIdx.x * kUbThreads + tid] = s;
+}
+
 // One dependent MFMA chain per wave with NV independent vector operations after each MFMA
 // (in eight chains of their own: fp32 FMAs, or exponentials when EXP), the MFMA's
 // accumulator in VGPRs (the compiler's form) or in AGPRs (inline asm, as the attention
@@ -230,6 +256,13 @@ FA_EXPORT int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* strea
   if (!out || blocks < 1 || iters < 1) return FA_UB_ERR_INVALID_ARG;
   hipLaunchKernelGGL(fa::ub_mfma_kernel, dim3(blocks), dim3(fa::kUbThreads), 0, static_cast<hipStream_t>(stream),
                      out, iters);
+  return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
+}
+
+FA_EXPORT int fa_ubench_mfma_fp8(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return FA_UB_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fa::ub_mfma_fp8_kernel, dim3(blocks), dim3(fa::kUbThreads), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
   return hipGetLastError() == hipSuccess ? FA_UB_OK : FA_UB_ERR_HIP;
 }
 

@@ -35,6 +35,11 @@ int fa_device_info(int device, int* compute_units, int* max_clock_khz, int* l2_b
  * (32768 FLOP each) in four independent chains. out: blocks * 256 floats (written). */
 int fa_ubench_mfma_bf16(float* out, int blocks, int iters, void* stream);
 
+/* The same with the 8-bit MFMA of the FP8 forward: each wave issues 8 * iters
+ * v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit block scales, 131072 FLOP each)
+ * in four independent chains. out: blocks * 256 floats (written). */
+int fa_ubench_mfma_fp8(float* out, int blocks, int iters, void* stream);
+
 /* `blocks` workgroups of 256 lanes; each lane runs 8 * iters vector operations in eight
  * independent chains: op 0 the exponential v_exp_f32, op 1 an fp32 FMA (2 FLOP).
  * out: blocks * 256 floats (written). */

@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
 
 def test_measurement_header_declares_its_calls():
     assert declared_functions([os.path.join(ROOT, "include", "fa_ubench.h")]) == [
-        "fa_device_info", "fa_ubench_copy", "fa_ubench_lds", "fa_ubench_mfma_bf16", "fa_ubench_mfma_mix", "fa_ubench_mfma_valu",
+        "fa_device_info", "fa_ubench_copy", "fa_ubench_lds", "fa_ubench_mfma_bf16", "fa_ubench_mfma_fp8", "fa_ubench_mfma_mix", "fa_ubench_mfma_valu",
         "fa_ubench_valu"]
 
 
@@ -314,6 +314,9 @@ def test_ubench_argument_checks():
     _lib()
     assert fa.fa_ubench_mfma_bf16(None, 1, 1, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_mfma_bf16(A, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_fp8(None, 1, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_fp8(A, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_ubench_mfma_fp8(A, 1, 0, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_valu(A, 1, 0, 0, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_valu(A, 1, 1, 2, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_ubench_lds(A, 1, 1, 5, None) == fa.FA_ERR_INVALID_ARG
