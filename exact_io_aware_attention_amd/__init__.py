@@ -31,7 +31,7 @@ __all__ = [
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
-FA_BWD_NOALLOC_MAX_SCRATCH = 16 << 20   # bytes of fa_bwd_noalloc's fixed device array (include/fa.h)
+FA_BWD_NOALLOC_MAX_SCRATCH = (16 << 20) + 256   # bytes of fa_bwd_noalloc's fixed device array (include/fa.h)
 FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -48,12 +48,15 @@ int check_common(int batch, int heads, int seqlen, int head_dim, float scale, in
   return FA_OK;
 }
 
-// D and -LSE / scale: one fp32 each per (head, token), each array rounded up to 256 bytes.
+// D and -LSE / scale: one fp32 each per (head, token), each array rounded up to 256 bytes,
+// then 256 bytes of work counters for the dK/dV kernel.
 size_t stat_bytes_for(int heads, long long tokens) {
   const size_t bytes = (size_t)heads * (size_t)tokens * sizeof(float);
   return ((bytes + 255) / 256) * 256;
 }
-size_t workspace_bytes_for(int heads, long long tokens) { return 2 * stat_bytes_for(heads, tokens); }
+constexpr size_t kCounterBytes = 256;
+static_assert(fa::kKvCounters * sizeof(int) <= kCounterBytes, "the counters fit their block");
+size_t workspace_bytes_for(int heads, long long tokens) { return 2 * stat_bytes_for(heads, tokens) + kCounterBytes; }
 
 // Checks shared by the backward entry points; sets pr.dvec to the workspace.
 int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
@@ -65,6 +68,7 @@ int check_bwd(fa::Problem& pr, void* workspace, size_t workspace_bytes, int batc
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FA_ERR_WORKSPACE;
   pr.dvec = static_cast<float*>(workspace);
   pr.mneg = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_bytes_for(heads, pr.total_tokens));
+  pr.kvctr = reinterpret_cast<int*>(static_cast<char*>(workspace) + 2 * stat_bytes_for(heads, pr.total_tokens));
   return FA_OK;
 }
 

@@ -89,6 +89,14 @@ __device__ __forceinline__ i32x8 f8_vt_operand(const uint8_t* Vs, int mt, int la
   return r;
 }
 
+// Wait states between the 64-cycle 8-bit MFMA that last wrote acc and any vector read of
+// it. The compiler's own count (about 19) proved too short for the last registers of the
+// accumulator (measured: a copy placed right after read them stale), so reads that can
+// follow the final P V closely go behind this fence.
+__device__ __forceinline__ void f8_acc_fence(f32x16& acc) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(acc));
+}
+
 template <int D>
 struct F8State {
   static constexpr int NT = D / 64, NM = D / 32;
@@ -249,6 +257,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int SROWS = 32 * stage_pitch<D>();  // u16 elements of one wave's staging
   static_assert(2 * SROWS * 2 <= L::BUF, "two waves' staging fits in one tile buffer");
   u16* stg = reinterpret_cast<u16*>(w < 2 ? buf0 : buf1) + (w & 1) * SROWS;
+  // the barrier above can pass at once for the last wave to arrive, right after its P V
+  f8_acc_fence(st.oacc[NM - 1]);
   const float l_tot = pair_sum(st.l_run);
   stage_acc_rows<D>(stg, st.oacc, p.descale_v / l_tot, lr, g);
   store_staged_rows<D, 32>(stg, p.o + base + (size_t)wq0 * stride, stride, len - wq0, lane);

@@ -23,6 +23,9 @@ struct Problem {
   float* mneg;         // backward workspace: -LSE_i / scale, same layout as lse
   float* dqacc;        // fused backward workspace: fp32 dQ accumulator (lse rows + 64) x head_dim,
                        // zeroed by launch_bwd_pre when set
+  int* kvctr;          // backward workspace: kKvCounters work counters of the head_dim-128 dK/dV
+                       // kernel, zeroed by the statistics kernels (launch_bwd_pre, the dQ pass
+                       // with statistics) and left zero by the dK/dV kernel when it ends
   const int32_t* cu_seqlens;  // NULL: padded batch
   int batch, heads, seqlen, head_dim;
   int total_tokens;    // batch * seqlen, or the packed token count
@@ -30,6 +33,9 @@ struct Problem {
   bool causal;
   hipStream_t stream;
 };
+
+// Work counters of the persistent dK/dV kernel: one per XCD and one of finished workgroups.
+constexpr int kKvCounters = 9;
 
 // Each launcher enqueues one kernel on p.stream and returns hipGetLastError().
 hipError_t launch_fwd_bf16(const Problem& p);

@@ -91,8 +91,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * scratch memory; a caller-owned workspace keeps the library free of allocations.)
  * Bytes of device workspace fa_bwd needs: two fp32 row statistics per (head, query
  * row), D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale, each array rounded up to
- * 256 bytes. For a packed batch (varlen != 0) pass total_tokens; otherwise it is
- * ignored. Returns 0 for invalid sizes.
+ * 256 bytes, then 256 bytes of work counters that the dK/dV stage hands its key tiles out
+ * with (written by the statistics stage, back to zero when the dK/dV stage ends). For a
+ * packed batch (varlen != 0) pass total_tokens; otherwise it is ignored. Returns 0 for
+ * invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int batch, int heads, int seqlen, int head_dim,
                               int varlen, int total_tokens);
@@ -154,7 +156,7 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
  * workspace, the same kernels and results. The row statistics go to a fixed device array
  * inside the library instead, FA_BWD_NOALLOC_MAX_SCRATCH bytes per GPU, held from the
  * library's first use on that GPU until the process ends; problems needing more than that
- * (8 * heads * tokens bytes, tokens = batch * seqlen or total_tokens: up to 2^21
+ * (8 * heads * tokens + 256 bytes, tokens = batch * seqlen or total_tokens: up to 2^21
  * (head, token) pairs, e.g. 32 heads x 65536 tokens) return FA_ERR_SCRATCH without
  * launching. No call allocates (no hipMalloc, no allocating library routine); the first
  * call on a device looks up the array's device address once (hipGetSymbolAddress), on
@@ -163,7 +165,7 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
  * one GPU (two streams, two threads) race and give wrong results; calls in stream order
  * are safe.
  */
-#define FA_BWD_NOALLOC_MAX_SCRATCH (16u << 20)
+#define FA_BWD_NOALLOC_MAX_SCRATCH ((16u << 20) + 256u)
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse,
                    void* dq, void* dk, void* dv,
@@ -176,8 +178,10 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * The stages of the backward, callable on their own (same arguments, conventions and
  * workspace as fa_bwd). The workspace statistics are written either by
  * fa_bwd_preprocess or by fa_bwd_dq_stats, which must complete before fa_bwd_dkdv (and
- * fa_bwd_dq) start; fa_bwd_dkdv and fa_bwd_dq only read the workspace and may run
- * concurrently on different streams. Each enqueues exactly one kernel, except
+ * fa_bwd_dq) start; fa_bwd_dq only reads the workspace and may run concurrently with
+ * fa_bwd_dkdv on a different stream. fa_bwd_dkdv also uses the workspace's work counters
+ * (it leaves them as it found them, zero), so two fa_bwd_dkdv calls must not share a
+ * workspace at the same time. Each enqueues exactly one kernel, except
  * fa_bwd_dq_stats with FA_DTYPE_FP32 (two).
  *
  *  fa_bwd_preprocess: workspace <- D_i = sum_k dO_ik * O_ik and -LSE_i / softmax_scale
@@ -186,8 +190,9 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  *    de guardar"). The second array is the starting value of the S = Q K^T
  *    accumulation in fa_bwd_dkdv, so that P = exp2(scale * log2(e) * (S - LSE / scale))
  *    needs no per-row term afterwards.
- *  fa_bwd_dkdv: dk, dv. One workgroup per (sequence, head, key tile) accumulates dK and
- *    dV on chip while walking the query tiles, recomputing P from lse.
+ *  fa_bwd_dkdv: dk, dv. Each (sequence, head, key tile) is taken by one workgroup, which
+ *    accumulates dK and dV on chip while walking the query tiles, recomputing P from lse
+ *    (at head_dim 128 one persistent workgroup per compute unit takes tile after tile).
  *  fa_bwd_dq: dq. One workgroup per (sequence, head, query tile) accumulates dQ on chip
  *    while walking the key tiles, recomputing P from lse.
  */

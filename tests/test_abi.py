@@ -177,8 +177,8 @@ def _atomic(**kw):
     (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
     (dict(workspace=None), fa.FA_ERR_WORKSPACE),
     (dict(workspace=A + 16), fa.FA_ERR_WORKSPACE),
-    # room for fa_bwd's statistics but not for the accumulator
-    (dict(workspace_bytes=2 * 256), fa.FA_ERR_WORKSPACE),
+    # room for fa_bwd's statistics and work counters but not for the accumulator
+    (dict(workspace_bytes=3 * 256), fa.FA_ERR_WORKSPACE),
     (dict(cu_seqlens=A, total_tokens=0), fa.FA_OK),
 ])
 def test_atomic_bwd_argument_checks(kw, code):
@@ -190,10 +190,10 @@ def test_atomic_workspace_size():
     _lib()
     # fa_bwd's statistics, then (heads * tokens + 64) rows of head_dim fp32
     assert fa.fa_bwd_atomic_workspace_bytes(4, 32, 4096, 128, 0, 0) == (
-        2 * 4 * 32 * 4096 * 4 + (32 * 4 * 4096 + 64) * 128 * 4)
-    assert fa.fa_bwd_atomic_workspace_bytes(1, 2, 16, 128, 0, 0) == 2 * 256 + (2 * 16 + 64) * 128 * 4
+        2 * 4 * 32 * 4096 * 4 + 256 + (32 * 4 * 4096 + 64) * 128 * 4)
+    assert fa.fa_bwd_atomic_workspace_bytes(1, 2, 16, 128, 0, 0) == 2 * 256 + 256 + (2 * 16 + 64) * 128 * 4
     assert fa.fa_bwd_atomic_workspace_bytes(7, 32, 2048, 128, 1, 16384) == (
-        2 * 32 * 16384 * 4 + (32 * 16384 + 64) * 128 * 4)
+        2 * 32 * 16384 * 4 + 256 + (32 * 16384 + 64) * 128 * 4)
     assert fa.fa_bwd_atomic_workspace_bytes(1, 1, 1, 80, 0, 0) == 0
     assert _atomic(workspace_bytes=fa.fa_bwd_atomic_workspace_bytes(1, 2, 16, 128, 0, 0) - 4) == fa.FA_ERR_WORKSPACE
 
@@ -201,9 +201,10 @@ def test_atomic_workspace_size():
 def test_workspace_size():
     _lib()
     # two fp32 arrays (D and -LSE / scale), each rounded up to 256 bytes
-    assert fa.fa_bwd_workspace_bytes(4, 32, 4096, 128, 0, 0) == 2 * 4 * 32 * 4096 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 3, 5, 64, 0, 0) == 2 * 256
-    assert fa.fa_bwd_workspace_bytes(7, 32, 2048, 128, 1, 16384) == 2 * 32 * 16384 * 4
+    # two statistics arrays (each rounded up to 256 bytes), then 256 bytes of work counters
+    assert fa.fa_bwd_workspace_bytes(4, 32, 4096, 128, 0, 0) == 2 * 4 * 32 * 4096 * 4 + 256
+    assert fa.fa_bwd_workspace_bytes(1, 3, 5, 64, 0, 0) == 2 * 256 + 256
+    assert fa.fa_bwd_workspace_bytes(7, 32, 2048, 128, 1, 16384) == 2 * 32 * 16384 * 4 + 256
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 80, 0, 0) == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64, 0, 0) == 0
 
@@ -359,4 +360,4 @@ def _noalloc(**kw):
 def test_noalloc_argument_checks(kw, code):
     _lib()
     assert _noalloc(**kw) == code
-    assert fa.FA_BWD_NOALLOC_MAX_SCRATCH == 16 << 20
+    assert fa.FA_BWD_NOALLOC_MAX_SCRATCH == (16 << 20) + 256

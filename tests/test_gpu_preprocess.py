@@ -2,7 +2,9 @@
 and the dQ pass that forms them itself (fa_bwd_dq_stats, what fa_bwd runs), write
 (D_i = sum_k dO_ik O_ik of the stored O, then -LSE_i / scale, each an fp32 array in the
 LSE layout starting on a 256-byte boundary) against the oracle's backward statistics,
-element by element.
+element by element; and the work counters behind them (256 bytes the dK/dV stage hands
+its key tiles out with): zero after either producer, zero again after every dK/dV call,
+so that dK/dV called twice on one workspace gives the same bits.
 
 Bound for D: the kernel forms exact products of bf16 values and adds them in fp32, so
 |D - D_ref| <= n u sum_k |dO_ik O_ik| with n = head_dim terms and u = 2^-24; 1e-5 covers
@@ -48,7 +50,7 @@ def test_preprocess_matches_oracle(case, producer):
     lse = (torch.randn(lse_shape, generator=g) * 4.0).float()
     scale = 0.0883883
     ws_bytes = fa.fa_bwd_workspace_bytes(B, H, N, d, int(cu is not None), T)
-    assert ws_bytes == 2 * _stat_bytes(H, T)
+    assert ws_bytes == 2 * _stat_bytes(H, T) + 256
     ws = torch.full((ws_bytes,), 0xA5, device="cuda", dtype=torch.uint8)
     od, dod, lsed = o.cuda(), do.cuda(), lse.cuda()
     cud = torch.tensor(cu, dtype=torch.int32, device="cuda") if cu is not None else None
@@ -78,3 +80,55 @@ def test_preprocess_matches_oracle(case, producer):
     err_d = np.abs(dvec - d_ref)
     assert np.all(err_d <= 1e-5 * mag + 1e-30), f"{label}: D off by {err_d.max()} (worst ratio {(err_d / (mag + 1e-30)).max()})"
     np.testing.assert_allclose(mneg, m_ref, rtol=2.0 ** -23, atol=0)
+    # the nine work counters of the dK/dV stage start at zero (the rest of the block is unused)
+    ctr = raw[2 * off: 2 * off + 36].view(torch.int32)
+    assert torch.all(ctr == 0), f"{label}: counters {ctr.tolist()}"
+
+
+DKDV_CASES = [
+    # (label, batch, seqlen, heads, cu_seqlens, causal)
+    ("d128 causal ragged", 2, 333, 3, None, 1),
+    ("d128 non-causal", 1, 700, 4, None, 0),
+    ("d128 packed", 3, 257, 2, [0, 100, 101, 358], 1),
+    ("d128 packed with empty key tiles", 4, 600, 2, [0, 600, 610, 1000, 1130], 1),
+]
+
+
+@pytest.mark.parametrize("case", DKDV_CASES, ids=[c[0] for c in DKDV_CASES])
+def test_dkdv_twice_on_one_workspace(case):
+    label, B, N, H, cu, causal = case
+    print(f"dK/dV twice: {label}", flush=True)
+    d = 128
+    g = torch.Generator().manual_seed(5 + N + H)
+    T = cu[-1] if cu is not None else B * N
+    shape = (T, H, d) if cu is not None else (B, N, H, d)
+    q, k, v, do = (torch.randn(shape, generator=g).to(torch.bfloat16).cuda() for _ in range(4))
+    cud = torch.tensor(cu, dtype=torch.int32, device="cuda") if cu is not None else None
+    cup = cud.data_ptr() if cud is not None else None
+    lse_shape = (H, T) if cu is not None else (B, H, N)
+    o = torch.empty_like(q)
+    lse = torch.empty(lse_shape, device="cuda", dtype=torch.float32)
+    scale = d ** -0.5
+    bf = fa.FA_DTYPE_BF16
+    sp = torch.cuda.current_stream().cuda_stream
+    assert fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
+                     causal, cup, T, bf, sp) == fa.FA_OK
+    ws_bytes = fa.fa_bwd_workspace_bytes(B, H, N, d, int(cu is not None), T)
+    ws = torch.full((ws_bytes,), 0xA5, device="cuda", dtype=torch.uint8)
+    dq = torch.empty_like(q)
+    assert fa.fa_bwd_dq_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              ws.data_ptr(), ws_bytes, dq.data_ptr(), B, H, N, d, scale, causal, cup, T, bf,
+                              sp) == fa.FA_OK
+    off = 2 * _stat_bytes(H, T)
+    runs = []
+    for _ in range(2):
+        dk, dv = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+        assert fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                              ws_bytes, dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, causal, cup, T, bf,
+                              sp) == fa.FA_OK
+        torch.cuda.synchronize()
+        ctr = ws[off: off + 36].cpu().view(torch.int32)
+        assert torch.all(ctr == 0), f"{label}: counters left at {ctr.tolist()}"
+        assert torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all(), f"{label}: rows left unwritten"
+        runs.append((dk.cpu(), dv.cpu()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1]), label
