@@ -218,17 +218,19 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u
   if (mask) fwd_mask<CAUSAL>(s1, k0 + 32, len, wq0, lane);
 
   // P_0 V_0 with exp(S_1). If block 1 then moves the reference, P_0 (formed under the
-  // old one) has joined O already and is scaled with the rest of it.
+  // old one) has joined O already and is scaled with the rest of it. Step i accumulates
+  // output block i % NB over key half i / NB: consecutive MFMAs never share an
+  // accumulator, so none waits for the result of the one before it.
   ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
   nb = st.m_run == -INFINITY ? 0.f : -st.m_run * c;
   {
     bf16x8 a[TP];
 #pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, i & 1, lane);
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i % NB, i / NB, lane);
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, (i + kFwdPf) & 1, lane);
-      st.oacc[i >> 1] = mfma32(a[i], p0[i & 1], st.oacc[i >> 1]);
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) % NB, (i + kFwdPf) / NB, lane);
+      st.oacc[i % NB] = mfma32(a[i], p0[i / NB], st.oacc[i % NB]);
 #pragma unroll
       for (int u = 0; u < 16 / TP; ++u) fwd_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
       step_fence();
@@ -242,11 +244,11 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u
   {
     bf16x8 a[TP];
 #pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i >> 1, 2 + (i & 1), lane);
+    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i % NB, 2 + i / NB, lane);
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) >> 1, 2 + ((i + kFwdPf) & 1), lane);
-      st.oacc[i >> 1] = mfma32(a[i], p1[i & 1], st.oacc[i >> 1]);
+      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) % NB, 2 + (i + kFwdPf) / NB, lane);
+      st.oacc[i % NB] = mfma32(a[i], p1[i / NB], st.oacc[i % NB]);
       step_fence();
     }
   }

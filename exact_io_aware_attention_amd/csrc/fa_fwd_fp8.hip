@@ -112,13 +112,12 @@ __device__ __forceinline__ void f8_tile(F8State<D>& st, const uint8_t* Ks, const
                                         int qi, int lane, float c, bool mask) {
   constexpr int NT = D / 64, NM = D / 32;
   const int g = lane >> 5;
-  f32x16 s[2];
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  // the two blocks' products alternate, so no MFMA waits for the one just before it
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    s[j] = f32x16{};
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) s[j] = mfma_fp8(f8_k_operand(Ks, j, t, lane), st.qf[t], s[j]);
-  }
+    for (int j = 0; j < 2; ++j) s[j] = mfma_fp8(f8_k_operand(Ks, j, t, lane), st.qf[t], s[j]);
   if (mask) {  // wave-uniform: a diagonal or tail tile
 #pragma unroll
     for (int j = 0; j < 2; ++j)
