@@ -133,7 +133,11 @@ __device__ __forceinline__ void fwd_exp_one(const f32x16& sj, f32x8& ev, bf16x8 
   // them out of the matrix-pipe phase they are meant to overlap.
   asm volatile("" : "+v"(e));
   ev[r & 7] = e;
-  ls[r & 3] += e;
+  // the first four start the partial sums (0 + e would cost an add: e may be -0)
+  if (r < 4)
+    ls[r & 3] = e;
+  else
+    ls[r & 3] += e;
   if (r % 8 == 7) {
     pj[r / 8] = to_bf16x8(ev);
     asm volatile("" : "+v"(pj[r / 8]));
@@ -166,7 +170,7 @@ __device__ __forceinline__ void fwd_redo(FwdState<D>& st, const f32x16& sj, bf16
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     ev[r & 7] = fast_exp2(fmaf(sj[r], c, nb));
-    sum += ev[r & 7];
+    sum = r == 0 ? ev[0] : sum + ev[r & 7];
     if (r % 8 == 7) pj[r / 8] = to_bf16x8(ev);
   }
   bsum = sum;
