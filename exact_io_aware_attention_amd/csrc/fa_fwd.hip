@@ -182,19 +182,32 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u
                                          int lane, float c, bool mask) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int TP = 2 * NB;  // PV steps per key block
+  constexpr int NSTEP = 2 * NS + 2 * TP;
   static_assert(16 % NS == 0 && 16 % TP == 0, "exponentials must split evenly over the steps");
+  // The tile's 2 NS + 2 TP MFMA operands from LDS, in step order (S_0, S_1, P_0 V_0,
+  // P_1 V_1) as one stream read kFwdPf steps ahead across the phase boundaries, so that
+  // no phase starts by waiting for its first reads.
+  auto op = [&](int n) {
+    if (n < NS) return fwd_k_operand<D>(Ks, 0, n, lane);
+    if (n < 2 * NS) return fwd_k_operand<D>(Ks, 1, n - NS, lane);
+    if (n < 2 * NS + TP) return fwd_v_operand<D>(Vs, (n - 2 * NS) % NB, (n - 2 * NS) / NB, lane);
+    return fwd_v_operand<D>(Vs, (n - 2 * NS - TP) % NB, 2 + (n - 2 * NS - TP) / NB, lane);
+  };
+  bf16x8 ring[kFwdPf];
+#pragma unroll
+  for (int n = 0; n < kFwdPf; ++n) ring[n] = op(n);
+  auto next = [&](int n) {
+    const bf16x8 a = ring[n % kFwdPf];
+    if (n + kFwdPf < NSTEP) ring[n % kFwdPf] = op(n + kFwdPf);
+    return a;
+  };
   f32x16 s0 = f32x16{}, s1 = f32x16{};
   // S_0
-  {
-    bf16x8 a[NS];
 #pragma unroll
-    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 0, s, lane);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 0, s + kFwdPf, lane);
-      s0 = mfma32(a[s], st.qf[s], s0);
-      step_fence();
-    }
+  for (int s = 0; s < NS; ++s) {
+    const bf16x8 a = next(s);
+    s0 = mfma32(a, st.qf[s], s0);
+    step_fence();
   }
   if (mask) fwd_mask<CAUSAL>(s0, k0, len, wq0, lane);  // wave-uniform: a diagonal or tail tile
 
@@ -203,18 +216,13 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u
   f32x8 ev;
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
   float nb = st.m_run == -INFINITY ? 0.f : -st.m_run * c;
-  {
-    bf16x8 a[NS];
 #pragma unroll
-    for (int s = 0; s < kFwdPf; ++s) a[s] = fwd_k_operand<D>(Ks, 1, s, lane);
+  for (int s = 0; s < NS; ++s) {
+    const bf16x8 a = next(NS + s);
+    s1 = mfma32(a, st.qf[s], s1);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + kFwdPf < NS) a[s + kFwdPf] = fwd_k_operand<D>(Ks, 1, s + kFwdPf, lane);
-      s1 = mfma32(a[s], st.qf[s], s1);
-#pragma unroll
-      for (int u = 0; u < 16 / NS; ++u) fwd_exp_one(s0, ev, p0, ls, nb, c, s * (16 / NS) + u);
-      step_fence();
-    }
+    for (int u = 0; u < 16 / NS; ++u) fwd_exp_one(s0, ev, p0, ls, nb, c, s * (16 / NS) + u);
+    step_fence();
   }
   float bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   if (!fwd_keep(st.m_run, s0, bsum)) fwd_redo<D>(st, s0, p0, bsum, c);
@@ -227,34 +235,24 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const u16* Ks, const u
   // accumulator, so none waits for the result of the one before it.
   ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
   nb = st.m_run == -INFINITY ? 0.f : -st.m_run * c;
-  {
-    bf16x8 a[TP];
 #pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i % NB, i / NB, lane);
+  for (int i = 0; i < TP; ++i) {
+    const bf16x8 a = next(2 * NS + i);
+    st.oacc[i % NB] = mfma32(a, p0[i / NB], st.oacc[i % NB]);
 #pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) % NB, (i + kFwdPf) / NB, lane);
-      st.oacc[i % NB] = mfma32(a[i], p0[i / NB], st.oacc[i % NB]);
-#pragma unroll
-      for (int u = 0; u < 16 / TP; ++u) fwd_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
-      step_fence();
-    }
+    for (int u = 0; u < 16 / TP; ++u) fwd_exp_one(s1, ev, p1, ls, nb, c, i * (16 / TP) + u);
+    step_fence();
   }
   bsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   if (!fwd_keep(st.m_run, s1, bsum)) fwd_redo<D>(st, s1, p1, bsum, c);
   st.l_run += bsum;
 
   // P_1 V_1
-  {
-    bf16x8 a[TP];
 #pragma unroll
-    for (int i = 0; i < kFwdPf; ++i) a[i] = fwd_v_operand<D>(Vs, i % NB, 2 + i / NB, lane);
-#pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      if (i + kFwdPf < TP) a[i + kFwdPf] = fwd_v_operand<D>(Vs, (i + kFwdPf) % NB, 2 + (i + kFwdPf) / NB, lane);
-      st.oacc[i % NB] = mfma32(a[i], p1[i / NB], st.oacc[i % NB]);
-      step_fence();
-    }
+  for (int i = 0; i < TP; ++i) {
+    const bf16x8 a = next(2 * NS + TP + i);
+    st.oacc[i % NB] = mfma32(a, p1[i / NB], st.oacc[i % NB]);
+    step_fence();
   }
 }
 
