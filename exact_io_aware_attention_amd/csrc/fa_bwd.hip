@@ -1449,6 +1449,10 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
         av = nv;
       }
     }
+    // the dQ products' first two K operands, read while the softmax below runs
+    bf16x8 ta[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ta[i] = swz_tr_operand<D>(Ks, 32 * j + 16 * (i / NB), 32 * (i % NB), lane);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, -st.lse2));
     if (mask) {  // wave-uniform: a diagonal or tail tile
@@ -1461,14 +1465,12 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - st.dd);
     const bf16x8 ds0 = to_bf16x8(half_of(dpacc, 0)), ds1 = to_bf16x8(half_of(dpacc, 1));
-    bf16x8 a = swz_tr_operand<D>(Ks, 32 * j, 0, lane);
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
-      const int bb = i >> 1, h = i & 1;
-      bf16x8 na = a;
-      if (i + 1 < 2 * NB) na = swz_tr_operand<D>(Ks, 32 * j + 16 * ((i + 1) & 1), 32 * ((i + 1) >> 1), lane);
+      const int bb = i % NB, h = i / NB;
+      const bf16x8 a = ta[i % 2];
+      if (i + 2 < 2 * NB) ta[i % 2] = swz_tr_operand<D>(Ks, 32 * j + 16 * ((i + 2) / NB), 32 * ((i + 2) % NB), lane);
       st.dqT[bb] = mfma32(a, h ? ds1 : ds0, st.dqT[bb]);
-      a = na;
     }
   }
 }
