@@ -1456,11 +1456,10 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const u16* buf, int k0, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, -st.lse2));
     if (mask) {  // wave-uniform: a diagonal or tail tile
+      // hidden: keys past the last one this query sees (one compare per score)
+      const int lim = (CAUSAL ? min(qi, len - 1) : len - 1) - k0 - 4 * g;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * j + crow_nat(r, g);
-        sacc[r] = (key >= len || (CAUSAL && key > qi)) ? 0.f : sacc[r];
-      }
+      for (int r = 0; r < 16; ++r) sacc[r] = 32 * j + crow_nat(r, 0) > lim ? 0.f : sacc[r];
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - st.dd);

@@ -117,11 +117,13 @@ __device__ __forceinline__ float row_max16(const f32x16& x) {
 template <bool CAUSAL>
 __device__ __forceinline__ void fwd_mask(f32x16& sj, int kb0, int len, int wq0, int lane) {
   const int qi = wq0 + (lane & 31), g = lane >> 5;
+  // Key kb0 + crow_nat(r, g) is hidden when it lies past the last key this query sees
+  // (the sequence's last, and under causal masking the query's own position): one
+  // compare of the register's lane-independent row offset against a per-lane bound.
+  const int last = CAUSAL ? min(qi, len - 1) : len - 1;
+  const int lim = last - kb0 - 4 * g;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = kb0 + crow_nat(r, g);
-    sj[r] = (key >= len || (CAUSAL && key > qi)) ? -INFINITY : sj[r];
-  }
+  for (int r = 0; r < 16; ++r) sj[r] = crow_nat(r, 0) > lim ? -INFINITY : sj[r];
 }
 
 // Exponential r of the block (the raw scores stay), its share of the row sum and, every

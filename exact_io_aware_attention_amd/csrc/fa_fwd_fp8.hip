@@ -119,13 +119,12 @@ __device__ __forceinline__ void f8_tile(F8State<D>& st, const uint8_t* Ks, const
 #pragma unroll
     for (int j = 0; j < 2; ++j) s[j] = mfma_fp8(f8_k_operand(Ks, j, t, lane), st.qf[t], s[j]);
   if (mask) {  // wave-uniform: a diagonal or tail tile
+    // hidden: keys past the last one this query sees (one compare per score)
+    const int lim = (CAUSAL ? min(qi, len - 1) : len - 1) - k0 - 4 * g;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * j + crow_nat(r, g);
-        s[j][r] = (key >= len || (CAUSAL && key > qi)) ? -INFINITY : s[j][r];
-      }
+      for (int r = 0; r < 16; ++r) s[j][r] = 32 * j + crow_nat(r, 0) > lim ? -INFINITY : s[j][r];
   }
   float mx = -INFINITY;
 #pragma unroll
