@@ -51,7 +51,7 @@ CSRC = os.path.join(ROOT, "exact_io_aware_attention_amd", "csrc")
 # kernel's sources hash to the value they had when the counters were taken; else null.
 TRAFFIC = {
     ("c3", "fwd"): {"read_bytes": 503496832, "write_bytes": 136314880, "factor": 1.0,
-                  "sources_sha256": "1ebe895394c792ff450a5581166f05da46c330fc2da985ced238948c274cd0b8",
+                  "sources_sha256": "3273f60472fad0d613cfddf8eb09ddc58614d7a4ded4f456c1bd667c5fefd26e",
                   "profile": "profiles/attention_fwd_bwd_c3.md"},
     ("c3", "bwd_dq"): {"read_bytes": 785595456, "write_bytes": 138412096, "factor": 1.0,
                   "sources_sha256": "b446bb7000ef9a451b97c7a1865b0bca6512193d1f73b33394e2c8a4926a3304",

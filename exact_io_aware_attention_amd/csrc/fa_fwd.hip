@@ -75,10 +75,10 @@ struct FwdState {
 // under the lazy rescale each block's softmax update stands on its own, so the
 // exponentials of one block run while the matrix pipe works on the other:
 //   S_0 | S_1 with exp(S_0) | P_0 V_0 with exp(S_1) | P_1 V_1
-// In each phase, operand reads run kPf steps ahead of the MFMA that uses them, and a
-// scheduling barrier (step_fence) closes every step, so the compiler neither sinks a
-// read next to its use (exposing the LDS latency) nor hoists all of them (a register
-// per read).
+// Operand reads run kFwdPf steps ahead of the MFMA that uses them, across the phase
+// boundaries, and a scheduling barrier (step_fence) closes every step, so the compiler
+// neither sinks a read next to its use (exposing the LDS latency) nor hoists all of
+// them (a register per read).
 
 constexpr int kFwdPf = 3;
 
