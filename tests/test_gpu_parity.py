@@ -80,6 +80,37 @@ def test_peaky_softmax(d, causal):
     full_parity(inp, causal, w.scale, "bf16", f"peaky d{d} c{int(causal)}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_growing_along_keys(d, causal):
+    """Every query gets a common component u (a +-1 pattern per head) and the keys drift
+    along u with their position, so the scores of each later key block exceed the running
+    reference by far more than 2^8: the forward moves its reference (its uncommon path)
+    on most blocks instead of on a query tile's first one only. Only O and LSE are held to
+    the contract: the reference moves are the forward's, and with rows this close to
+    one-hot each dS = P (dP - D) is a difference of nearly equal terms (D comes from the
+    bf16 O), so the gradients' relative error says nothing here (as with identical keys)."""
+    w = _w("bf16", d, causal)
+    inp = W.make_inputs(w, seed=91, batch=1, seqlen=600, heads=2)
+    n = inp.k.shape[1]
+    u = torch.sign(inp.q[:, :1].float())
+    inp.q.copy_((inp.q.float() + 0.5 * u).to(inp.q.dtype))
+    drift = 0.05 * torch.arange(n, dtype=torch.float32)[None, :, None, None] * u
+    inp.k.copy_((inp.k.float() + drift).to(inp.k.dtype))
+    # The claim above, counted on the scores themselves (log2 units, 32-key blocks, the
+    # causal limit ignored): how often a block's maximum exceeds everything before it by
+    # more than the 2^8 bound of the row-sum check.
+    q, k = f64(inp.q)[0], f64(inp.k)[0]
+    s2 = np.einsum("qhd,khd->hqk", q, k) * w.scale / np.log(2.0)
+    blocks = s2[:, :, : (n // 32) * 32].reshape(s2.shape[0], s2.shape[1], -1, 32).max(axis=3)
+    before = np.maximum.accumulate(blocks, axis=2)[:, :, :-1]
+    assert np.mean(blocks[:, :, 1:] - before > 8.0) > 0.5
+    o, lse, _, _, _ = run_gpu(inp, causal, w.scale)
+    o_ref, lse_ref = oracle.forward(inp.q, inp.k, inp.v, w.scale, causal)
+    check(f"growing d{d} c{int(causal)} O", "bf16", o, o_ref, "o")
+    check(f"growing d{d} c{int(causal)} LSE", "bf16", lse, lse_ref, "lse")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_identical_keys(causal):
     """All keys equal: uniform weights, O is the (prefix) mean of V. The exact dQ is
